@@ -1,0 +1,190 @@
+"""FP64 CPU oracle for attention forward and row softmax.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``.  The product library never imports,
+links or calls anything here, and nothing here imports the product package.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, compiled with
+gcc into ``liboracle.so``).  This module only turns fp16 / bf16 / fp32 input
+bits into exact float64 arrays and calls the C entry points.
+
+Definitions followed (see the header of ``oracle.c`` for the stage-by-stage
+statement):
+
+* attention: "CUDA FlashAttention: from online softmax to long-sequence IO
+  limits" (chengzipai.xyz), section 1 (O = softmax(QK^T/sqrt(D) + M)V, causal
+  mask j <= i) and section 3 (the naive three stages);
+* row softmax: the softmax kernel study (lpnh.cn/news/2830604), section 3.1
+  (double-precision stable softmax as the CPU reference).
+
+Pins: every function here is checked in ``tests/test_oracle.py`` against
+closed forms, invariants and independent library routines.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_I64 = ctypes.c_int64
+_PD = ctypes.POINTER(ctypes.c_double)
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = False) -> str:
+    """Compile ``liboracle.so`` with gcc (host code only; no GPU involved)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    lib.oracle_attn_fwd.argtypes = [_PD, _PD, _PD, _PD, _PD, _I64, _I64, _I64, _I64,
+                                    ctypes.c_int, ctypes.c_int]
+    lib.oracle_attn_fwd.restype = ctypes.c_int
+    lib.oracle_attn_rows.argtypes = [_PD, _PD, _PD, _I64, _I64, _I64, _I64, ctypes.c_int,
+                                     _PI64, _I64, _PD, _PD, ctypes.c_int]
+    lib.oracle_attn_rows.restype = ctypes.c_int
+    lib.oracle_attn_scores.argtypes = [_PD, _PD, _I64, _I64, ctypes.c_int, _I64, _PD]
+    lib.oracle_attn_scores.restype = ctypes.c_int64
+    lib.oracle_row_softmax.argtypes = [_PD, _PD, _I64, _I64, ctypes.c_int]
+    lib.oracle_row_softmax.restype = ctypes.c_int
+    lib.oracle_row_softmax_rows.argtypes = [_PD, _I64, _I64, _PI64, _I64, _PD,
+                                            ctypes.c_int]
+    lib.oracle_row_softmax_rows.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            _lib = _bind(_LIB)
+    return _lib
+
+
+def swap_library(path: str | None):
+    """Point this module at another build of the oracle (None: the default one).
+
+    Used by the tests that plant mistakes in a copy of oracle.c and check that
+    the pins catch them.  Returns nothing; not thread-safe.
+    """
+    global _lib
+    with _lock:
+        _lib = None if path is None else _bind(path)
+
+
+def default_threads() -> int:
+    """Threads the oracle uses: the host's cores, at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+# --------------------------------------------------------------- conversions
+
+def to_f64(a) -> np.ndarray:
+    """Exact float64 copy of a host array or CPU torch tensor.
+
+    fp16 and fp32 convert through numpy; bf16 is widened by placing its 16
+    bits in the high half of an fp32 word, which is exact.
+    """
+    if hasattr(a, "detach"):  # torch tensor (CPU)
+        import torch
+        t = a.detach().contiguous()
+        if t.dtype == torch.bfloat16:
+            bits = t.view(torch.int16).numpy().astype(np.uint16)
+            return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        a = t.numpy()
+    a = np.asarray(a)
+    if a.dtype == np.float64:
+        return np.ascontiguousarray(a)
+    return np.ascontiguousarray(a.astype(np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_PD)
+
+
+# ----------------------------------------------------------------- attention
+
+def attn_fwd(q, k, v, causal: bool, nthreads: int | None = None):
+    """O [B,H,N,D] and LSE [B,H,N] in float64 for inputs [B,H,N,D]."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    B, H, N, D = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    o = np.empty((B, H, N, D), np.float64)
+    lse = np.empty((B, H, N), np.float64)
+    rc = _load().oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
+                                 int(bool(causal)), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_attn_fwd failed (%d)" % rc)
+    return o, lse
+
+
+def attn_rows(q, k, v, causal: bool, rows, nthreads: int | None = None):
+    """O and LSE for selected rows only; rows are flat ids (b*H+h)*N+i.
+
+    Returns o [len(rows), D] and lse [len(rows)] in float64.
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    B, H, N, D = q.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    o = np.empty((rows.size, D), np.float64)
+    lse = np.empty((rows.size,), np.float64)
+    rc = _load().oracle_attn_rows(_ptr(q), _ptr(k), _ptr(v), B, H, N, D, int(bool(causal)),
+                                  rows.ctypes.data_as(_PI64), rows.size, _ptr(o), _ptr(lse),
+                                  nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_attn_rows failed (%d)" % rc)
+    return o, lse
+
+
+def attn_scores(q, k, causal: bool, i: int) -> np.ndarray:
+    """Stage 1 alone: the scaled scores of query row i of one head ([N,D] inputs)."""
+    q, k = to_f64(q), to_f64(k)
+    N, D = q.shape
+    s = np.empty((N,), np.float64)
+    n = _load().oracle_attn_scores(_ptr(q), _ptr(k), N, D, int(bool(causal)), int(i), _ptr(s))
+    if n < 0:
+        raise RuntimeError("oracle_attn_scores failed")
+    return s[:n].copy()
+
+
+# --------------------------------------------------------------- row softmax
+
+def row_softmax(x, nthreads: int | None = None) -> np.ndarray:
+    """y = softmax over the last axis of a 2-D x, in float64."""
+    x = to_f64(x)
+    M, N = x.shape
+    y = np.empty((M, N), np.float64)
+    rc = _load().oracle_row_softmax(_ptr(x), _ptr(y), M, N, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_row_softmax failed (%d)" % rc)
+    return y
+
+
+def row_softmax_rows(x, rows, nthreads: int | None = None) -> np.ndarray:
+    """Softmax of the selected rows of x; returns [len(rows), N] float64."""
+    x = to_f64(x)
+    M, N = x.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    y = np.empty((rows.size, N), np.float64)
+    rc = _load().oracle_row_softmax_rows(_ptr(x), M, N, rows.ctypes.data_as(_PI64), rows.size,
+                                         _ptr(y), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_row_softmax_rows failed (%d)" % rc)
+    return y

@@ -1,0 +1,273 @@
+/*
+ * FP64 CPU oracle for exact scaled-dot-product attention and row softmax.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no code, header or table with the HIP path.
+ *
+ * What it computes (plain definitions, no blocking, no fusion, no online
+ * recurrence):
+ *
+ *   Attention, from "CUDA FlashAttention: from online softmax to long-sequence
+ *   IO limits" (chengzipai.xyz), section 1 (the definition of O and of the
+ *   causal mask) and section 3 (the naive three-stage path):
+ *     stage 1  s_ij = (sum_d q_id * k_jd) / sqrt(D)      for the keys j of row i
+ *     stage 2  m_i = max_j s_ij, p_ij = exp(s_ij - m_i), l_i = sum_j p_ij,
+ *              p_ij = p_ij / l_i                          (safe softmax)
+ *     stage 3  o_id = sum_j p_ij * v_jd
+ *   The causal mask keeps key j for query i iff j <= i (top-left aligned, Q
+ *   and K have the same length N), so every row has at least one key.  The
+ *   log-sum-exp of a row is lse_i = m_i + ln(l_i), the natural log of
+ *   sum_j exp(s_ij) over the same keys (the page's section 7 only says the
+ *   LSE is saved for the backward pass; this is the plain reading).
+ *
+ *   Row softmax, from the softmax kernel study (lpnh.cn/news/2830604),
+ *   section 3.1: a double-precision stable softmax per row,
+ *     m = max_j x_j, e_j = exp(x_j - m), d = sum_j e_j, y_j = e_j / d.
+ *
+ * Every sum runs in increasing index order, so results are deterministic for
+ * any thread count.  One query row is materialised at a time (a full score
+ * matrix at N = 8192 would be 512 MiB per head in FP64); that changes memory
+ * use only, not the arithmetic.
+ *
+ * Layouts: q, k, v, o are [B, H, N, D] row-major, element ((b*H+h)*N+n)*D+d;
+ * lse is [B, H, N]; x, y are [M, N] row-major.  All buffers are host memory
+ * owned by the caller.  Entry points return 0 on success, -1 on a bad
+ * argument (null pointer or non-positive size), -2 if a work buffer could not
+ * be allocated.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* ---------------------------------------------------------------- attention */
+
+/* Stage 1 for one query row i of one head: s_j for j in J_i, written to s[0..nkeys). */
+static int64_t scores_row(const double *q, const double *k, int64_t N, int64_t D,
+                          int causal, int64_t i, double *s)
+{
+    const int64_t nkeys = causal ? i + 1 : N;
+    const double root_d = sqrt((double)D);
+    const double *qi = q + i * D;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        const double *kj = k + j * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            dot += qi[d] * kj[d];
+        s[j] = dot / root_d;
+    }
+    return nkeys;
+}
+
+/* Stages 1-3 for one query row.  s is a work row of at least N doubles. */
+static void attn_row(const double *q, const double *k, const double *v, int64_t N,
+                     int64_t D, int causal, int64_t i, double *s, double *o_row,
+                     double *lse_out)
+{
+    const int64_t nkeys = scores_row(q, k, N, D, causal, i, s);
+
+    /* stage 2: safe softmax over the materialised row */
+    double m = s[0];
+    for (int64_t j = 1; j < nkeys; ++j)
+        if (s[j] > m)
+            m = s[j];
+    double l = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    for (int64_t j = 0; j < nkeys; ++j)
+        s[j] = s[j] / l;
+
+    /* stage 3: P times V */
+    for (int64_t d = 0; d < D; ++d)
+        o_row[d] = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        const double p = s[j];
+        const double *vj = v + j * D;
+        for (int64_t d = 0; d < D; ++d)
+            o_row[d] += p * vj[d];
+    }
+    *lse_out = m + log(l);
+}
+
+typedef struct {
+    const double *q, *k, *v;
+    double *o, *lse;
+    int64_t H, N, D;
+    int causal;
+    const int64_t *rows; /* flat row ids ((b*H+h)*N+i), or NULL for all rows */
+    int64_t nrows;
+    int64_t begin, end;  /* range of the row list this thread owns */
+    int status;
+} attn_job;
+
+static void *attn_worker(void *arg)
+{
+    attn_job *jb = (attn_job *)arg;
+    double *s = (double *)malloc((size_t)jb->N * sizeof(double));
+    if (!s) {
+        jb->status = -2;
+        return NULL;
+    }
+    for (int64_t r = jb->begin; r < jb->end; ++r) {
+        const int64_t flat = jb->rows ? jb->rows[r] : r;
+        const int64_t bh = flat / jb->N, i = flat % jb->N;
+        const int64_t head = bh * jb->N * jb->D;
+        attn_row(jb->q + head, jb->k + head, jb->v + head, jb->N, jb->D, jb->causal, i, s,
+                 jb->o + r * jb->D, jb->lse + r);
+    }
+    free(s);
+    jb->status = 0;
+    return NULL;
+}
+
+static int run_attn(const double *q, const double *k, const double *v, double *o,
+                    double *lse, int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                    const int64_t *rows, int64_t nrows, int nthreads)
+{
+    if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || N < 1 || D < 1 || nrows < 0)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if ((int64_t)nthreads > nrows)
+        nthreads = nrows > 0 ? (int)nrows : 1;
+    attn_job jobs[256];
+    pthread_t tid[256];
+    int started[256] = {0};
+    for (int t = 0; t < nthreads; ++t) {
+        attn_job jb = {q, k, v, o, lse, H, N, D, causal, rows, nrows,
+                       nrows * t / nthreads, nrows * (t + 1) / nthreads, -2};
+        jobs[t] = jb;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        started[t] = pthread_create(&tid[t], NULL, attn_worker, &jobs[t]) == 0;
+    attn_worker(&jobs[0]);
+    int status = jobs[0].status;
+    for (int t = 1; t < nthreads; ++t) {
+        if (started[t])
+            pthread_join(tid[t], NULL);
+        else
+            attn_worker(&jobs[t]); /* could not spawn: do the share here */
+        if (jobs[t].status != 0)
+            status = jobs[t].status;
+    }
+    return status;
+}
+
+/* All B*H*N rows: o is [B,H,N,D], lse is [B,H,N]. */
+int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o, double *lse,
+                    int64_t B, int64_t H, int64_t N, int64_t D, int causal, int nthreads)
+{
+    if (B < 1 || H < 1 || N < 1)
+        return -1;
+    return run_attn(q, k, v, o, lse, B, H, N, D, causal, NULL, B * H * N, nthreads);
+}
+
+/* Selected rows only: rows[r] = (b*H+h)*N+i; o_rows is [nrows,D], lse_rows is [nrows]. */
+int oracle_attn_rows(const double *q, const double *k, const double *v, int64_t B, int64_t H,
+                     int64_t N, int64_t D, int causal, const int64_t *rows, int64_t nrows,
+                     double *o_rows, double *lse_rows, int nthreads)
+{
+    if (!rows)
+        return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= B * H * N)
+            return -1;
+    return run_attn(q, k, v, o_rows, lse_rows, B, H, N, D, causal, rows, nrows, nthreads);
+}
+
+/* Stage 1 alone for one row of one head ([N,D] q and k): returns the key count. */
+int64_t oracle_attn_scores(const double *q, const double *k, int64_t N, int64_t D, int causal,
+                           int64_t i, double *s)
+{
+    if (!q || !k || !s || N < 1 || D < 1 || i < 0 || i >= N)
+        return -1;
+    return scores_row(q, k, N, D, causal, i, s);
+}
+
+/* -------------------------------------------------------------- row softmax */
+
+static void softmax_row(const double *x, double *y, int64_t N)
+{
+    double m = x[0];
+    for (int64_t j = 1; j < N; ++j)
+        if (x[j] > m)
+            m = x[j];
+    double d = 0.0;
+    for (int64_t j = 0; j < N; ++j) {
+        y[j] = exp(x[j] - m);
+        d += y[j];
+    }
+    for (int64_t j = 0; j < N; ++j)
+        y[j] = y[j] / d;
+}
+
+typedef struct {
+    const double *x;
+    double *y;
+    int64_t N;
+    const int64_t *rows;
+    int64_t begin, end;
+} sm_job;
+
+static void *sm_worker(void *arg)
+{
+    sm_job *jb = (sm_job *)arg;
+    for (int64_t r = jb->begin; r < jb->end; ++r) {
+        const int64_t src = jb->rows ? jb->rows[r] : r;
+        softmax_row(jb->x + src * jb->N, jb->y + r * jb->N, jb->N);
+    }
+    return NULL;
+}
+
+static int run_softmax(const double *x, double *y, int64_t N, const int64_t *rows,
+                       int64_t nrows, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if ((int64_t)nthreads > nrows)
+        nthreads = nrows > 0 ? (int)nrows : 1;
+    sm_job jobs[256];
+    pthread_t tid[256];
+    int started[256] = {0};
+    for (int t = 0; t < nthreads; ++t) {
+        sm_job jb = {x, y, N, rows, nrows * t / nthreads, nrows * (t + 1) / nthreads};
+        jobs[t] = jb;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        started[t] = pthread_create(&tid[t], NULL, sm_worker, &jobs[t]) == 0;
+    sm_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) {
+        if (started[t])
+            pthread_join(tid[t], NULL);
+        else
+            sm_worker(&jobs[t]);
+    }
+    return 0;
+}
+
+/* All M rows of x [M,N] into y [M,N]. */
+int oracle_row_softmax(const double *x, double *y, int64_t M, int64_t N, int nthreads)
+{
+    if (!x || !y || M < 1 || N < 1)
+        return -1;
+    return run_softmax(x, y, N, NULL, M, nthreads);
+}
+
+/* Selected rows: y_rows is [nrows,N], row r is softmax of x[rows[r], :]. */
+int oracle_row_softmax_rows(const double *x, int64_t M, int64_t N, const int64_t *rows,
+                            int64_t nrows, double *y_rows, int nthreads)
+{
+    if (!x || !y_rows || !rows || M < 1 || N < 1 || nrows < 0)
+        return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= M)
+            return -1;
+    return run_softmax(x, y_rows, N, rows, nrows, nthreads);
+}

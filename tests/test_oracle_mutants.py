@@ -1,0 +1,99 @@
+"""Planted mistakes in a copy of the oracle must be caught by the pins.
+
+Each case edits one line of a copy of oracle/oracle.c (on the CPU, in a
+temporary directory), builds it with gcc, points the oracle module at the
+copy, runs the pin tests of test_oracle.py against it and requires at least
+one of them to fail.  The real oracle is restored afterwards.  No edit makes
+the copy read outside its buffers.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "causal_off_by_one": ("causal ? i + 1 : N", "causal ? i : N"),
+    "scale_by_D": ("s[j] = dot / root_d;", "s[j] = dot / (double)D;"),
+    "scale_dropped": ("s[j] = dot / root_d;", "s[j] = dot;"),
+    "transposed_key": ("dot += qi[d] * kj[d];", "dot += qi[d] * k[d * N + j];"),
+    "lse_log2": ("*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
+    "lse_without_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
+    "k_used_as_v": ("const double *vj = v + j * D;", "const double *vj = k + j * D;"),
+    "attn_min_not_max": ("for (int64_t j = 1; j < nkeys; ++j)\n        if (s[j] > m)",
+                         "for (int64_t j = 1; j < nkeys; ++j)\n        if (s[j] < m)"),
+    "attn_no_max_subtraction": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+    "attn_not_normalised": ("s[j] = s[j] / l;", "s[j] = s[j];"),
+    "heads_mixed": ("const int64_t head = bh * jb->N * jb->D;", "const int64_t head = 0;"),
+    "softmax_no_max_subtraction": ("y[j] = exp(x[j] - m);", "y[j] = exp(x[j]);"),
+    "softmax_min_not_max": ("for (int64_t j = 1; j < N; ++j)\n        if (x[j] > m)",
+                            "for (int64_t j = 1; j < N; ++j)\n        if (x[j] < m)"),
+    "softmax_not_normalised": ("y[j] = y[j] / d;", "y[j] = y[j];"),
+    "softmax_rows_shifted": ("softmax_row(jb->x + src * jb->N", "softmax_row(jb->x + (src / 2) * jb->N"),
+}
+
+PIN_CALLS = [
+    (pins.test_stage1_picks_one_key_column, {"D": 16}),
+    (pins.test_stage1_causal_key_count_and_prefix, {}),
+    (pins.test_single_key_returns_v0, {"D": 64}),
+    (pins.test_identical_keys_give_prefix_mean, {"causal": True}),
+    (pins.test_zero_queries_give_uniform_weights, {"causal": False}),
+    (pins.test_two_keys_logistic, {"a": 7.0}),
+    (pins.test_large_logits_stay_finite, {}),
+    (pins.test_wide_logit_spread_needs_the_row_max, {}),
+    (pins.test_key_shift_invariance, {"causal": True}),
+    (pins.test_causal_prefix_property, {}),
+    (pins.test_linear_in_v_and_weights_convex, {}),
+    (pins.test_heads_and_batches_are_independent, {}),
+    (pins.test_lse_normalises_the_scores, {"causal": True}),
+    (pins.test_matches_torch_sdpa_float64, {"N": 33, "D": 64, "causal": True}),
+    (pins.test_softmax_rows_sum_to_one_and_shift_invariant, {}),
+    (pins.test_softmax_all_zero_is_uniform, {}),
+    (pins.test_softmax_special_last_element_closed_form, {}),
+    (pins.test_softmax_matches_library_routines, {}),
+]
+
+
+def _failures():
+    failed = []
+    for fn, kw in PIN_CALLS:
+        try:
+            fn(**kw)
+        except Exception:  # a failing assertion, a NaN comparison, an error return
+            failed.append(fn.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation site vanished: %r" % old
+    mutated = src.replace(old, new, 1)
+    c_path = tmp_path / "mutant.c"
+    c_path.write_text(mutated)
+    so_path = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", str(c_path),
+                    "-o", str(so_path), "-lm"], check=True)
+    oracle.swap_library(str(so_path))
+    try:
+        failed = _failures()
+    finally:
+        oracle.swap_library(None)
+    assert failed, "planted mistake %s passed every pin" % name
+
+
+def test_unmodified_copy_passes_every_pin(tmp_path):
+    so_path = tmp_path / "libcopy.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", SRC,
+                    "-o", str(so_path), "-lm"], check=True)
+    oracle.swap_library(str(so_path))
+    try:
+        failed = _failures()
+    finally:
+        oracle.swap_library(None)
+    assert failed == []

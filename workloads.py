@@ -1,0 +1,137 @@
+"""Seeded synthetic workloads shared by the tests, the smoke check and the benchmark.
+
+This module draws random inputs and describes workload shapes.  It holds none
+of the method's arithmetic: no scores, no softmax, no reductions.  Both the
+HIP path's callers and the oracle's callers take their inputs from here.
+
+Recipe (the same for every workload): a torch CPU ``Generator`` seeded with
+the workload's seed draws float32 ``randn`` for Q, then K, then V (in that
+order), each scaled by its standard deviation, then rounded to the storage
+dtype with torch's round-to-nearest-even cast.  Row-softmax inputs are float32
+``randn`` with the last element of every row overwritten by a special value
+(the softmax kernel study, lpnh.cn/news/2830604, section 3.3, tests rows
+whose last element is special; 80.0 forces the running maximum to jump at the
+very end of the row).
+
+The attention shapes follow "CUDA FlashAttention: from online softmax to
+long-sequence IO limits" (chengzipai.xyz), section 1: B=1, H=32, D=128 with N
+from 512 to 8192, causal fp16.  The row-softmax boundary shape M=1025, N=257
+is the softmax study's section 3.4 case.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    causal: bool
+    dtype: str          # "f16" or "bf16"
+    sigma_qk: float
+    sigma_v: float
+    seed: int
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic FLOP: 2BHN^2D causal, 4BHN^2D non-causal (section 1 of the FA page)."""
+        return attn_flops(self.B, self.H, self.N, self.D, self.causal)
+
+    def describe(self) -> str:
+        return "%s attn fwd %s B%d H%d N%d D%d" % (
+            "causal" if self.causal else "non-causal", self.dtype, self.B, self.H, self.N, self.D)
+
+
+@dataclass(frozen=True)
+class SoftmaxWorkload:
+    name: str
+    M: int
+    N: int
+    last: float
+    seed: int
+
+    @property
+    def bytes(self) -> float:
+        """Algorithmic bytes: read x once and write y once, fp32."""
+        return 8.0 * self.M * self.N
+
+    def describe(self) -> str:
+        return "row_softmax fp32 M%d N%d" % (self.M, self.N)
+
+
+def attn_flops(B: int, H: int, N: int, D: int, causal: bool) -> float:
+    return (2.0 if causal else 4.0) * B * H * N * N * D
+
+
+ATTN = {
+    "C1": AttnWorkload("C1", 1, 4, 256, 128, True, "f16", 1.0, 1.0, 43),
+    "C2": AttnWorkload("C2", 1, 32, 512, 128, True, "f16", 1.0, 1.0, 44),
+    "C3": AttnWorkload("C3", 1, 32, 2048, 128, True, "bf16", 3.0, 1.0, 45),
+    "C4": AttnWorkload("C4", 1, 32, 8192, 128, True, "f16", 1.0, 1.0, 46),
+    "C5": AttnWorkload("C5", 4, 32, 4095, 64, False, "bf16", 1.0, 1.0, 47),
+}
+
+SOFTMAX = {
+    "R1": SoftmaxWorkload("R1", 1025, 257, 80.0, 48),
+    "R2": SoftmaxWorkload("R2", 8192, 32768, 80.0, 49),
+}
+
+TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def attn_inputs(B: int, H: int, N: int, D: int, dtype: str, seed: int,
+                sigma_qk: float = 1.0, sigma_v: float = 1.0):
+    """Q, K, V as contiguous CPU tensors [B,H,N,D] of the storage dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    shape = (B, H, N, D)
+    td = TORCH_DTYPE[dtype]
+    q = (torch.randn(shape, generator=g, dtype=torch.float32) * sigma_qk).to(td)
+    k = (torch.randn(shape, generator=g, dtype=torch.float32) * sigma_qk).to(td)
+    v = (torch.randn(shape, generator=g, dtype=torch.float32) * sigma_v).to(td)
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def workload_inputs(w: AttnWorkload):
+    return attn_inputs(w.B, w.H, w.N, w.D, w.dtype, w.seed, w.sigma_qk, w.sigma_v)
+
+
+def softmax_inputs(M: int, N: int, seed: int, last: float | None = 80.0):
+    """x [M,N] float32 CPU tensor; the last element of each row set to ``last``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    x = torch.randn((M, N), generator=g, dtype=torch.float32)
+    if last is not None:
+        x[:, -1] = last
+    return x.contiguous()
+
+
+def sample_rows(B: int, H: int, N: int, count: int, seed: int):
+    """Flat row ids (b*H+h)*N+i to check at full size.
+
+    Always includes the first and last rows of the first and last heads and
+    rows around multiples of 64 (tile edges), plus seeded random rows.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    BH = B * H
+    count = min(count, BH * N)
+    picks = set()
+    for bh in {0, BH - 1}:
+        for i in {0, 1, N // 2, N - 2, N - 1}:
+            if 0 <= i < N:
+                picks.add(bh * N + i)
+    for e in range(64, N, max(64, (N // 8) // 64 * 64 or 64)):
+        bh = int(torch.randint(0, BH, (1,), generator=g))
+        for i in (e - 1, e):
+            if 0 <= i < N:
+                picks.add(bh * N + i)
+    while len(picks) < count:
+        picks.add(int(torch.randint(0, BH * N, (1,), generator=g)))
+    return sorted(picks)
