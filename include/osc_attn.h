@@ -1,0 +1,111 @@
+/*
+ * osc_attn.h - C ABI of the MI355X (gfx950) attention-forward and row-softmax
+ * library (libosc_attn.so).
+ *
+ * Two operations, both from the reference pages:
+ *
+ *   attn_fwd     exact scaled-dot-product attention forward,
+ *                O = softmax(Q K^T / sqrt(D) + M) V, with M the causal mask
+ *                (M_ij = 0 if j <= i, else -inf) or no mask.  Definition:
+ *                "CUDA FlashAttention: from online softmax to long-sequence IO
+ *                limits" (chengzipai.xyz), section 1; computed with the tiled
+ *                online-softmax recurrence of its section 4 (running max m,
+ *                running sum l, unnormalised FP32 output rescaled per K/V
+ *                tile), which reaches the same result as the plain definition
+ *                up to floating-point rounding.
+ *
+ *   row_softmax  y = softmax(x) along each row of an FP32 matrix, computed
+ *                with the online (m, d) recurrence and two-level merge of the
+ *                softmax kernel study (lpnh.cn/news/2830604), sections 4.4
+ *                and 4.6.  It shares its merge code with attn_fwd.
+ *
+ * Conventions (all entry points):
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates no memory, keeps no state between calls and never synchronises.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns at once.  Completion is observed with the caller's own stream or
+ *     event synchronisation; a fault during execution surfaces there.
+ *   - Arguments are validated before anything is enqueued.  On any error
+ *     nothing is enqueued and the outputs are left untouched.
+ *   - Tensors are dense and row-major (contiguous); the library cannot check
+ *     that the buffers are as large as the sizes say.
+ *   - Unsupported shapes are rejected, never answered approximately (FA page,
+ *     section 9: unsupported shapes must fall back explicitly rather than give
+ *     silently wrong results).
+ */
+#ifndef OSC_ATTN_H
+#define OSC_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same opaque type as HIP's hipStream_t. */
+typedef struct ihipStream_t *hipStream_t;
+
+/* Storage type of Q, K and V.  Arithmetic is FP32 in both cases: products on
+ * the matrix cores accumulate in FP32, and the softmax state (m, l) and the
+ * output accumulator are FP32 (FA page, section 2). */
+typedef enum {
+    ATTN_F16 = 0,  /* IEEE binary16 */
+    ATTN_BF16 = 1  /* bfloat16 */
+} attn_dtype_t;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = 2,       /* a size < 1, or sizes whose product overflows the limits below */
+    ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64 or 128, or unknown dtype */
+    ATTN_ERR_ALIGN = 4,       /* a pointer is not aligned as required below */
+    ATTN_ERR_LAUNCH = 5,      /* the HIP runtime refused the kernel launch */
+    ATTN_ERR_ALIAS = 6        /* an output buffer overlaps an input buffer */
+} attn_status_t;
+
+/*
+ * attn_fwd - attention forward for B*H independent heads.
+ *
+ *   q, k, v  [B, H, N, D] of `dtype`, contiguous: element (b,h,n,d) at
+ *            ((b*H + h)*N + n)*D + d.  16-byte aligned.
+ *   o        [B, H, N, D] FP32 output, same indexing, 16-byte aligned.
+ *            Row i of head (b,h) is sum_j p_ij v_j with p_ij the softmax
+ *            weights of the scaled logits s_ij = q_i . k_j / sqrt(D).
+ *   lse      [B, H, N] FP32 output, 4-byte aligned: the natural-log
+ *            log-sum-exp of the scaled logits of each row,
+ *            lse_i = ln sum_{j in J_i} exp(s_ij), kept for a backward pass
+ *            (FA page, section 7).
+ *   B, H, N  batch, heads, sequence length (Q and K/V have the same N).
+ *   D        head dimension: 64 or 128 (FA page, section 7, gives these two
+ *            dedicated layouts; other D return ATTN_ERR_UNSUPPORTED).
+ *   causal   nonzero: key j is visible to query i iff j <= i (top-left
+ *            aligned); zero: every key is visible.
+ *   dtype    ATTN_F16 or ATTN_BF16, the storage type of q, k and v.
+ *   stream   HIP stream to enqueue on.
+ *
+ * Limits: N*D < 2^31 and B*H*N*D < 2^62.  o and lse must not overlap q, k, v
+ * or each other.  The softmax scale is fixed at 1/sqrt(D).
+ */
+attn_status_t attn_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
+                       int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                       attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * row_softmax - y[r, :] = softmax(x[r, :]) for r < M.
+ *
+ *   x   [M, N] FP32 input, row-major, 4-byte aligned (rows need not be
+ *       16-byte aligned; misaligned row starts are handled inside).
+ *   y   [M, N] FP32 output, same layout; must not overlap x.
+ *   M   number of rows (>= 1);  N  row length (>= 1);  M*N < 2^62.
+ *   stream  HIP stream to enqueue on.
+ */
+attn_status_t row_softmax(const float *x, float *y, int64_t M, int64_t N, hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char *attn_status_str(attn_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSC_ATTN_H */

@@ -1,0 +1,132 @@
+"""Python binding of libosc_attn.so: attention forward and row softmax on MI355X.
+
+Argument marshalling only.  Every step of both operations runs in the HIP
+kernels of the shared library; there is no Python, PyTorch or CPU fallback.
+If the library has not been built (``python -m online_softmax_causal_amd.build``)
+``load()`` raises.
+
+The entry points mirror the C ABI in ``include/osc_attn.h``:
+
+    attn_fwd(q, k, v, o, lse, B, H, N, D, causal, dtype, stream=None)
+    row_softmax(x, y, M, N, stream=None)
+    attn_status_str(status)
+
+Pointer arguments accept device tensors (``torch.Tensor``, only its address is
+used) or plain integers.  ``stream`` accepts None (PyTorch's current stream on
+the current device), a ``torch.cuda.Stream`` or an integer handle.  A nonzero
+status raises ``AttnError``.  ``attention(q, k, v, causal)`` is a convenience
+wrapper that allocates O and LSE with PyTorch and calls ``attn_fwd``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libosc_attn.so")
+
+ATTN_F16 = 0
+ATTN_BF16 = 1
+STATUS = {
+    0: "ATTN_OK",
+    1: "ATTN_ERR_NULL",
+    2: "ATTN_ERR_SHAPE",
+    3: "ATTN_ERR_UNSUPPORTED",
+    4: "ATTN_ERR_ALIGN",
+    5: "ATTN_ERR_LAUNCH",
+    6: "ATTN_ERR_ALIAS",
+}
+EXPORTS = ("attn_fwd", "row_softmax", "attn_status_str")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, STATUS.get(status, status),
+                                          attn_status_str(status)))
+
+
+def load():
+    """Load libosc_attn.so and declare its signatures (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libosc_attn.so is not built: run "
+                           "`python -m online_softmax_causal_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.row_softmax.argtypes = [vp, vp, i64, i64, vp]
+    lib.row_softmax.restype = ctypes.c_int
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    raise TypeError("expected a tensor, an int address or None, got %r" % type(x))
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    raise TypeError("expected a stream handle, torch.cuda.Stream or None")
+
+
+def _dtype(d) -> int:
+    if isinstance(d, int):
+        return d
+    if isinstance(d, str):
+        return {"f16": ATTN_F16, "fp16": ATTN_F16, "float16": ATTN_F16,
+                "bf16": ATTN_BF16, "bfloat16": ATTN_BF16}[d]
+    import torch
+    return {torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}[d]
+
+
+def attn_status_str(status: int) -> str:
+    return load().attn_status_str(int(status)).decode()
+
+
+def attn_fwd(q, k, v, o, lse, B, H, N, D, causal, dtype, stream=None) -> None:
+    """Enqueue attention forward (see include/osc_attn.h); raises AttnError on a bad status."""
+    st = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N),
+                         int(D), int(bool(causal)), _dtype(dtype), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+
+
+def row_softmax(x, y, M, N, stream=None) -> None:
+    """Enqueue the row softmax of an FP32 [M, N] matrix; raises AttnError on a bad status."""
+    st = load().row_softmax(_ptr(x), _ptr(y), int(M), int(N), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "row_softmax")
+
+
+def attention(q, k, v, causal: bool, stream=None):
+    """O (FP32) and LSE (FP32) for contiguous device tensors q, k, v of shape [B, H, N, D]."""
+    import torch
+    B, H, N, D = q.shape
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous [B, H, N, D]")
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    o = torch.empty((B, H, N, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, B, H, N, D, causal, q.dtype, stream)
+    return o, lse

@@ -1,0 +1,64 @@
+// Host-side argument checks for the C ABI.  Pure C++: no HIP call, so every
+// rejection happens before anything touches the device (and can be exercised
+// on a machine without a GPU).
+#pragma once
+
+#include <cstdint>
+
+#include "osc_attn.h"
+
+namespace osc {
+
+// a*b for non-negative operands, false if it would reach 2^62.
+inline bool mul_below_2_62(int64_t a, int64_t b, int64_t* out) {
+    const int64_t lim = int64_t(1) << 62;
+    if (a != 0 && b > (lim - 1) / a) return false;
+    *out = a * b;
+    return true;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+inline attn_status_t validate_attn(const void* q, const void* k, const void* v, const float* o,
+                                   const float* lse, int64_t B, int64_t H, int64_t N, int64_t D,
+                                   attn_dtype_t dtype) {
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1 || D < 1) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    int64_t bh = 0, bhn = 0, total = 0, nd = 0;
+    if (!mul_below_2_62(B, H, &bh) || !mul_below_2_62(bh, N, &bhn) ||
+        !mul_below_2_62(bhn, D, &total) || !mul_below_2_62(N, D, &nd))
+        return ATTN_ERR_SHAPE;
+    if (nd >= (int64_t(1) << 31) || bh >= (int64_t(1) << 31)) return ATTN_ERR_SHAPE;
+    // One workgroup per 128-query tile at most: the grid must stay below 2^31.
+    if (bh * ((N + 127) / 128) >= (int64_t(1) << 31)) return ATTN_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(lse, 4))
+        return ATTN_ERR_ALIGN;
+    const int64_t in_bytes = total * 2, o_bytes = total * 4, lse_bytes = bhn * 4;
+    const void* ins[3] = {q, k, v};
+    for (const void* in : ins)
+        if (overlap(o, o_bytes, in, in_bytes) || overlap(lse, lse_bytes, in, in_bytes))
+            return ATTN_ERR_ALIAS;
+    if (overlap(o, o_bytes, lse, lse_bytes)) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+inline attn_status_t validate_softmax(const float* x, const float* y, int64_t M, int64_t N) {
+    if (!x || !y) return ATTN_ERR_NULL;
+    if (M < 1 || N < 1) return ATTN_ERR_SHAPE;
+    int64_t total = 0;
+    if (!mul_below_2_62(M, N, &total)) return ATTN_ERR_SHAPE;
+    if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return ATTN_ERR_SHAPE;
+    if (!aligned(x, 4) || !aligned(y, 4)) return ATTN_ERR_ALIGN;
+    if (overlap(x, total * 4, y, total * 4)) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+}  // namespace osc

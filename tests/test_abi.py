@@ -1,0 +1,111 @@
+"""The C ABI library on the CPU: it loads, exports what include/*.h declares,
+and rejects bad arguments before any HIP call (no kernel is launched here)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import online_softmax_causal_amd as osc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BASE = 1 << 40          # a 256-byte aligned address that is never dereferenced
+MB = 1 << 20
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(",
+                         text, flags=re.M):
+            if m.group(1) not in ("defined",):
+                names.add(m.group(1))
+    return names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = osc.load()
+    names = declared_functions()
+    assert {"attn_fwd", "row_softmax", "attn_status_str"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    for code in osc.STATUS:
+        s = osc.attn_status_str(code)
+        assert isinstance(s, str) and s
+    assert osc.attn_status_str(0) == "ok"
+    assert osc.attn_status_str(99) == "unknown status"
+
+
+def call_attn(q=BASE, k=BASE + 64 * MB, v=BASE + 128 * MB, o=BASE + 192 * MB,
+              lse=BASE + 320 * MB, B=1, H=2, N=64, D=128, causal=1, dtype=0):
+    lib = osc.load()
+    return lib.attn_fwd(q, k, v, o, lse, B, H, N, D, causal, dtype, None)
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_attn_rejects_null(field):
+    assert call_attn(**{field: None}) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(D=0), dict(N=-5),
+                                dict(N=1 << 24), dict(B=1 << 40, H=1 << 30)])
+def test_attn_rejects_bad_shapes(kw):
+    assert call_attn(**kw) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(D=96), dict(D=32), dict(D=256), dict(dtype=2), dict(dtype=-1)])
+def test_attn_rejects_unsupported(kw):
+    assert call_attn(**kw) == 3
+
+
+@pytest.mark.parametrize("kw", [dict(q=BASE + 8), dict(k=BASE + 64 * MB + 2),
+                                dict(v=BASE + 128 * MB + 4), dict(o=BASE + 192 * MB + 12),
+                                dict(lse=BASE + 320 * MB + 2)])
+def test_attn_rejects_misaligned(kw):
+    assert call_attn(**kw) == 4
+
+
+@pytest.mark.parametrize("kw", [dict(o=BASE), dict(lse=BASE + 64 * MB + 16),
+                                dict(o=BASE + 128 * MB - 64), dict(lse=BASE + 192 * MB + 256)])
+def test_attn_rejects_overlap(kw):
+    assert call_attn(**kw) == 6
+
+
+def call_softmax(x=BASE, y=BASE + 64 * MB, M=4, N=100):
+    return osc.load().row_softmax(x, y, M, N, None)
+
+
+def test_softmax_rejections():
+    assert call_softmax(x=None) == 1
+    assert call_softmax(y=None) == 1
+    assert call_softmax(M=0) == 2
+    assert call_softmax(N=0) == 2
+    assert call_softmax(M=1 << 40, N=1 << 30) == 2
+    assert call_softmax(x=BASE + 2) == 4
+    assert call_softmax(y=BASE + 64 * MB + 1) == 4
+    assert call_softmax(y=BASE + 200) == 6
+
+
+def test_python_binding_raises_with_status():
+    with pytest.raises(osc.AttnError) as e:
+        osc.attn_fwd(None, BASE, BASE, BASE, BASE, 1, 1, 1, 128, True, "f16", stream=0)
+    assert e.value.status == 1
+    with pytest.raises(osc.AttnError) as e:
+        osc.row_softmax(BASE, BASE + 2 * MB, 1, 0, stream=0)
+    assert e.value.status == 2
+
+
+def test_product_package_never_touches_the_oracle():
+    """The HIP path's sources import, link and call nothing under oracle/."""
+    pkg = os.path.dirname(osc.__file__)
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if os.path.isfile(path) and path.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+            text = open(path).read()
+            assert "oracle" not in text.lower(), path
