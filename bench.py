@@ -1,0 +1,389 @@
+"""Benchmark: causal attention forward TFLOP/s at B=1, H=32, N=8192, D=128, fp16.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+
+A step is one attn_fwd call (the whole hot path) over the workload, with
+inputs resident in HBM.  W untimed steps, then K steps timed between two
+device synchronisations; value = 2*B*H*N^2*D / (seconds per step) / 1e12.
+The FLOP count is the FA page's causal count (section 1 of "CUDA
+FlashAttention: from online softmax to long-sequence IO limits").
+
+One JSON line goes to stdout.  Besides the contract fields it carries:
+  roofline      achieved TFLOP/s of the attention kernel (events on the
+                launch stream around the timed region) against the MI355X dense
+                fp16 MFMA peak, and the HBM traffic rocprofv3 measured for the
+                same kernel (profiles/attn_fwd_C4_traffic.txt) when that
+                measurement was taken on the current kernel source;
+  cpu_baseline  the FP64 oracle timed on this host's cores on a bounded
+                sample of the same workload (every s-th query row);
+  parity_sample max-abs error of the GPU output on those sampled rows;
+  extra         the other configurations (C1, C2, C3, C5 attention; R1, R2
+                row softmax), timed as the median of 7 group means of
+                back-to-back launches (FA page, section 8 method).
+Runs on one GPU only; --gpus above 1 exits with a message.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6      # MI355X dense fp16/bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "online_softmax_causal_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_C4_traffic.txt")
+COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("attn_fwd.hip", "online_merge.hpp"):
+        with open(os.path.join(ROOT, "online_softmax_causal_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    if it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def time_groups(fn, stream, groups=7, min_ms=2.0):
+    """Median (and min) over 7 groups of the mean time of R back-to-back calls (ms)."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-6) * 1e3
+    reps = max(5, int(min_ms / one) + 1)
+    means = []
+    for _ in range(groups):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        means.append(a.elapsed_time(b) / reps)
+    means.sort()
+    return means[len(means) // 2], means[0]
+
+
+def extra_configs(dev):
+    import torch
+    import online_softmax_causal_amd as osc
+    import workloads
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name in ("C1", "C2", "C3", "C5"):
+        w = workloads.ATTN[name]
+        q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
+        o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        fn = lambda: osc.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.D, w.causal, w.dtype)
+        med, mn = time_groups(fn, stream)
+        tf = w.flops / (med * 1e-3) / 1e12
+        out[name] = {"workload": w.describe(), "ms": round(med, 5), "ms_min": round(mn, 5),
+                     "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+        del q, k, v, o, lse
+    for name in ("R1", "R2"):
+        w = workloads.SOFTMAX[name]
+        x = workloads.softmax_inputs(w.M, w.N, seed=w.seed, last=w.last).to(dev)
+        y = torch.empty_like(x)
+        fn = lambda: osc.row_softmax(x, y, w.M, w.N)
+        med, mn = time_groups(fn, stream)
+        gbs = w.bytes / (med * 1e-3) / 1e9
+        out[name] = {"workload": w.describe(), "ms": round(med, 5), "ms_min": round(mn, 5),
+                     "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        del x, y
+    return out
+
+
+def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, target_s=15.0):
+    """Time the FP64 oracle on every s-th query row of the workload.
+
+    A calibration run on a small sample fixes s so the timed sample takes
+    about target_s seconds.  FLOP of a sample are counted row by row with the
+    same convention as the metric: a causal row i costs 4*(i+1)*D.
+    """
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    qd, kd, vd = oracle.to_f64(q), oracle.to_f64(k), oracle.to_f64(v)
+    total_rows = w.B * w.H * w.N
+
+    def row_flops(rows):
+        i = np.asarray(rows) % w.N
+        keys = (i + 1) if w.causal else np.full_like(i, w.N)
+        return float((4.0 * keys * w.D).sum())
+
+    def run(stride):
+        rows = np.arange(stride // 2, total_rows, stride, dtype=np.int64)
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.attn_rows(qd, kd, vd, w.causal, rows, nthreads=threads)
+        return rows, time.perf_counter() - t0, o_ref, lse_ref
+
+    stride = 1024
+    rows, secs, _, _ = run(stride)
+    rate = row_flops(rows) / secs
+    want = rate * target_s
+    stride = int(max(1, min(total_rows, round(row_flops(range(total_rows)) / want))))
+    rows, secs, o_ref, lse_ref = run(stride)
+    flops = row_flops(rows)
+    o_rows = o_gpu.reshape(-1, w.D)[rows]
+    lse_rows = lse_gpu.reshape(-1)[rows]
+    parity = {"rows": int(len(rows)),
+              "max_abs_o": float(np.abs(o_rows - o_ref).max()),
+              "max_abs_lse": float(np.abs(lse_rows - lse_ref).max())}
+    base = {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d query rows (every %d-th flat row of %s), %.3g FLOP in %.1f s, "
+                      "FP64 three-stage oracle" % (len(rows), total_rows, stride, w.describe(),
+                                                   flops, secs)}
+    return base, parity
+
+
+def profile_pass():
+    """The program rocprofv3 wraps for the counter passes: 3 launches of the C4
+    attention kernel, then 3 plain device copies of COPY_BYTES (torch's copy
+    kernel) whose HBM traffic is known (read COPY_BYTES, write COPY_BYTES)."""
+    import torch
+    import online_softmax_causal_amd as osc
+    import workloads
+    dev = torch.device("cuda:0")
+    w = workloads.ATTN["C4"]
+    q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
+    o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        osc.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.D, w.causal, w.dtype)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("profile pass done", flush=True)
+
+
+def _pmc_rows(path):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % path)
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(rows, counter, match):
+    vals = {}
+    for r in rows:
+        if r.get("Counter_Name") == counter and match(r.get("Kernel_Name", "")):
+            vals.setdefault(r.get("Dispatch_Id"), 0.0)
+            vals[r.get("Dispatch_Id")] += float(r["Counter_Value"])
+    return [vals[k] for k in sorted(vals, key=lambda x: int(x))]
+
+
+def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
+    """Write profiles/attn_fwd_C4_traffic.txt from two rocprofv3 --pmc runs of --profile-pass."""
+    import workloads
+    w = workloads.ATTN["C4"]
+    is_attn = lambda n: "attn_fwd_kernel" in n
+    is_copy = lambda n: "attn_fwd_kernel" not in n
+    fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    a_fetch = _per_dispatch(fr, "FETCH_SIZE", is_attn)
+    c_fetch = _per_dispatch(fr, "FETCH_SIZE", is_copy)
+    a_write = _per_dispatch(wr, "WRITE_SIZE", is_attn)
+    c_write = _per_dispatch(wr, "WRITE_SIZE", is_copy)
+    # steady-state launches: skip the first of each kind
+    mean = lambda xs: sum(xs[1:]) / max(1, len(xs) - 1) if len(xs) > 1 else xs[0]
+    kib_c_fetch, kib_c_write = mean(c_fetch[-3:]), mean(c_write[-3:])
+    f_scale = COPY_BYTES / (kib_c_fetch * 1024.0)
+    w_scale = COPY_BYTES / (kib_c_write * 1024.0)
+    a_read = mean(a_fetch) * 1024.0 * f_scale
+    a_written = mean(a_write) * 1024.0 * w_scale
+    compulsory = 3 * w.B * w.H * w.N * w.D * 2 + w.B * w.H * w.N * (w.D + 1) * 4
+    text = "\n".join([
+        "attn_fwd_kernel, causal fp16 B1 H32 N8192 D128: HBM traffic per launch (rocprofv3 --pmc)",
+        "",
+        "commands (from the repository root, TMPDIR=/tmp):",
+        "  " + cmd_fetch,
+        "  " + cmd_write,
+        "  python bench.py --summarize-traffic <fetch_dir> <write_dir>",
+        "",
+        "attention FETCH_SIZE per dispatch (KiB): " + ", ".join("%.0f" % x for x in a_fetch),
+        "attention WRITE_SIZE per dispatch (KiB): " + ", ".join("%.0f" % x for x in a_write),
+        "copy kernel (%d bytes read + %d written) FETCH_SIZE (KiB): %s" % (
+            COPY_BYTES, COPY_BYTES, ", ".join("%.0f" % x for x in c_fetch)),
+        "copy kernel WRITE_SIZE (KiB): " + ", ".join("%.0f" % x for x in c_write),
+        "calibration: read scale %.4f, write scale %.4f (known bytes / counter bytes of the copy)" % (
+            f_scale, w_scale),
+        "",
+        "hbm_read_bytes_per_launch: %.6g" % a_read,
+        "hbm_write_bytes_per_launch: %.6g" % a_written,
+        "hbm_bytes_per_launch: %.6g" % (a_read + a_written),
+        "compulsory_bytes (Q,K,V read once; O fp32 + LSE written once): %.6g" % compulsory,
+        "kernel_source_sha256_16: %s" % kernel_source_hash(),
+        "",
+    ])
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def summarize_trace(trace_dir, out_path, cmd, last):
+    """Write a kernel-duration summary from a rocprofv3 --kernel-trace --stats csv run.
+
+    Reports rocprofv3's own per-kernel statistics and, for the attention
+    kernel, the mean over the last `last` launches (the timed steps).
+    """
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats or not trace:
+        raise SystemExit("no kernel_stats.csv / kernel_trace.csv under %s" % trace_dir)
+    lines = ["rocprofv3 kernel statistics", "", "command (from the repository root, TMPDIR=/tmp):",
+             "  " + cmd, "", "kernel | calls | average us | min us | max us | share %"]
+    with open(stats[0]) as f:
+        for r in csv.DictReader(f):
+            lines.append("%s | %s | %.2f | %.2f | %.2f | %s" % (
+                r["Name"][:110], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, r["Percentage"]))
+    durs = {}
+    with open(trace[0]) as f:
+        for r in csv.DictReader(f):
+            durs.setdefault(r["Kernel_Name"], []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    lines.append("")
+    for name, d in durs.items():
+        if "attn_fwd_kernel" in name or "softmax" in name:
+            d.sort()
+            tail = [x[1] for x in d[-last:]]
+            lines.append("%s: mean of the last %d launches (the timed steps) %.2f us" % (
+                name[:110], len(tail), sum(tail) / len(tail) / 1e3))
+    lines.append("kernel_source_sha256_16: %s" % kernel_source_hash())
+    lines.append("")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="run the fixed launch sequence the counter passes profile")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
+    ap.add_argument("--trace-last", type=int, default=20)
+    ap.add_argument("--cmd", default="")
+    ap.add_argument("--cmd-fetch", default="")
+    ap.add_argument("--cmd-write", default="")
+    args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.cmd, args.trace_last)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
+                          args.cmd_fetch, args.cmd_write)
+        return
+    if args.profile_pass:
+        profile_pass()
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import online_softmax_causal_amd as osc
+    import workloads
+
+    osc.load()
+    dev = torch.device("cuda:0")
+    w = workloads.ATTN["C4"]
+    q, k, v = workloads.workload_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.full((w.B, w.H, w.N, w.D), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        osc.attn_fwd(qd, kd, vd, o, lse, w.B, w.H, w.N, w.D, w.causal, w.dtype, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    o_host = o.cpu().double().numpy()
+    lse_host = lse.cpu().double().numpy()
+
+    traffic = measured_traffic()
+    line = {
+        "metric": "causal attn fwd TFLOP/s (2BHN²D) at H=32,D=128,N=8192; % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+                   "causal": w.causal, "inputs": "Q,K,V iid N(0,1) rounded to fp16, seed %d" % w.seed,
+                   "output": "O fp32 [B,H,N,D], LSE fp32 [B,H,N]"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                     "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
+                     "kernel": "attn_fwd_kernel<f16, D=128, causal>",
+                     "kernel_source_sha256_16": kernel_source_hash()},
+    }
+    if not args.no_cpu:
+        base, parity = cpu_baseline(w, q, k, v, o_host, lse_host)
+        line["cpu_baseline"] = base
+        line["parity_sample"] = parity
+    if not args.no_extra:
+        line["extra"] = extra_configs(dev)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
