@@ -36,11 +36,33 @@ def _compile(src: str) -> str:
     return obj
 
 
+def check_m0(src: str = "attn_fwd.hip") -> None:
+    """The attention kernel writes M0 in inline assembly (the LDS address of
+    global_load_lds_dwordx4).  That is only safe while no compiler-generated
+    instruction uses M0, so check the generated gfx950 assembly: every M0
+    reference must be one of those writes, directly followed by the copy."""
+    asm = os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
+    cmd = [HIPCC] + FLAGS + ["-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", asm]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc -S failed on %s:\n%s" % (src, r.stderr))
+    lines = [ln.split(";")[0].strip() for ln in open(asm)]
+    lines = [ln for ln in lines if ln]
+    for i, ln in enumerate(lines):
+        if "m0" in ln.replace(",", " ").split():
+            ok = ln.startswith("s_mov_b32 m0,") and i + 1 < len(lines) and \
+                lines[i + 1].startswith("global_load_lds_dwordx4")
+            if not ok:
+                raise RuntimeError("unexpected use of M0 in %s: %r" % (src, ln))
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        m0 = ex.submit(check_m0)
         objs = list(ex.map(_compile, SOURCES))
+        m0.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

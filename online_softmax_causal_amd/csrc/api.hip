@@ -14,9 +14,9 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, float* o, fl
     const attn_status_t st = osc::validate_attn(q, k, v, o, lse, B, H, N, D, dtype);
     if (st != ATTN_OK) return st;
     const int64_t BH = B * H;
-    const int qb = osc::attn_pick_qb(BH, N);
+    const int waves = osc::attn_pick_waves(BH, N);
     const hipError_t e = osc::launch_attn_fwd(q, k, v, o, lse, (int)BH, (int)N, (int)D,
-                                              causal != 0, dtype == ATTN_BF16, qb, stream);
+                                              causal != 0, dtype == ATTN_BF16, waves, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -55,8 +55,14 @@ typedef unsigned short u16;
 template <bool BF16>
 struct Mma;
 
+// kSumRounded: whether the row sum l is taken over the 16-bit P fed to the
+// P V product (fp16: rounding error <= 2^-11 relative, so numerator and
+// denominator stay consistent and the LSE error stays below 5e-4) or over the
+// FP32 P before rounding (bf16: its 2^-9 rounding would move the LSE by up to
+// 2e-3 on rows dominated by one key).
 template <>
 struct Mma<false> {
+    static constexpr bool kSumRounded = true;
     __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -68,10 +74,16 @@ struct Mma<false> {
         r[1] = (_Float16)hi;
         return __builtin_bit_cast(unsigned, r);
     }
+    // acc + lo + hi of one packed dword, accumulated in FP32.
+    __device__ __forceinline__ static float sum2(unsigned packed, float acc) {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
+    }
 };
 
 template <>
 struct Mma<true> {
+    static constexpr bool kSumRounded = false;
     __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -82,42 +94,66 @@ struct Mma<true> {
         r[1] = (__bf16)hi;
         return __builtin_bit_cast(unsigned, r);
     }
+    __device__ __forceinline__ static float sum2(unsigned packed, float acc) {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+    }
 };
 
 // Compile-time geometry of one kernel instance.
-template <int D_, int QB_, int NW_>
+//
+// LDS holds STAGES stages; a stage is one K tile followed by one V tile, each
+// BC = 64 key rows of D 16-bit values, unpadded (a row is D/8 chunks of 16
+// bytes).  Tiles are written straight from global memory by
+// global_load_lds_dwordx4, which puts lane i's 16 bytes at 16*i past a
+// wave-uniform LDS address, so one wave instruction fills one 1 KiB block
+// (RPB rows).  Bank conflicts are avoided by storing logical chunk c of row r
+// at chunk position c ^ chunk_swizzle(r): the swizzle gives the 16
+// consecutive rows read by one ds_read_b128 phase 16 distinct 16-byte bank
+// groups, and the 4 rows x 4 chunks of one 32-lane ds_read_b64_tr_b16 phase
+// 16 distinct bank groups as well.
+template <int D_, int NW_, int STAGES_, int DIST_>
 struct Geo {
     static constexpr int D = D_;
-    static constexpr int QB = QB_;              // 32-row query blocks per wave
-    static constexpr int NW = NW_;              // waves per workgroup
+    static constexpr int NW = NW_;              // waves per workgroup, 32 query rows each
+    static constexpr int STAGES = STAGES_;      // LDS stages
+    static constexpr int DIST = DIST_;          // tiles copied ahead of the one being computed
     static constexpr int THREADS = 64 * NW;
-    static constexpr int BR = 32 * QB * NW;     // query rows per workgroup
-    static constexpr int BC = D == 128 ? 64 : 128;  // keys per LDS tile
-    static constexpr int SUB = 64;              // keys per compute step
-    // LDS pitches in 16-bit elements.  K: pitch = D/2 + 4 dwords, an odd
-    // multiple of 4 modulo 64 banks, so the 16 lanes of one ds_read_b128
-    // phase (16 consecutive key rows) hit 16 distinct 4-bank groups.  V:
-    // pitch = D/2 + 16 dwords, 16 or 48 modulo 64, so the four key rows that
-    // each 16-lane group of a ds_read_b64_tr_b16 touches land in disjoint
-    // banks, also across the two d-halves of a 32-lane phase.
-    static constexpr int KP = D + 8;
-    static constexpr int VP = D + 32;
-    static constexpr int KT = BC * KP;
-    static constexpr int VT = BC * VP;
-    static constexpr int STAGE = KT + VT;
-    static constexpr int CHUNKS = BC * D / 8;   // 16-byte chunks per K (or V) tile
-    static constexpr int CPT = CHUNKS / THREADS;
-    static_assert(CHUNKS % THREADS == 0, "tile fill must divide evenly");
-    static_assert(BC % SUB == 0, "compute step must divide the tile");
+    static constexpr int BR = 32 * NW;          // query rows per workgroup
+    static constexpr int BC = 64;               // keys per tile
+    static constexpr int MT = D / 32;           // 32-row d blocks of O^T
+    static constexpr int KS = D / 16;           // 16-wide d steps of Q K^T
+    static constexpr int CPR = D / 8;           // 16-byte chunks per row
+    static constexpr int RPB = 1024 / (2 * D);  // rows per 1 KiB block
+    static constexpr int TILE = BC * D;         // 16-bit elements per K (or V) tile
+    static constexpr int STAGE = 2 * TILE;
+    static constexpr int BPW = BC / RPB / NW;   // 1 KiB blocks per wave per tile
+    static_assert(BPW >= 1 && BPW * RPB * NW == BC, "tile fill must divide evenly");
+    static_assert(DIST == 1 || DIST == 2, "prefetch distance");
 };
 
-template <int D, int QB>
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+    if constexpr (D == 128)
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    else
+        return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+template <int D>
 struct WaveState {
-    u32x4 qf[QB][D / 16];     // Q^T fragments (MFMA B operand), one per 16-wide d step
-    f32x16 acc[QB][D / 32];   // O^T accumulators, 32 d-rows each
-    float m[QB];              // running max of this lane's query, log2 units
-    float l[QB];              // this lane's share of the running sum
+    u32x4 qf[D / 16];     // Q^T fragments (MFMA B operand), one per 16-wide d step
+    f32x16 acc[D / 32];   // O^T accumulators, 32 d-rows each
+    float m;              // reference max of this lane's query, log2 units
+    float l;              // this lane's share of the running sum (relative to m)
 };
+
+// Conditional rescaling: the reference max m moves only when a query's
+// tile max exceeds it by more than 2^8.  Between moves the exponentials are
+// taken against a stale m, so each P element is at most 2^8 (exact in fp16
+// and bf16 range); O and l always share the same reference, so O = o/l is
+// unchanged.  This skips the rescale of the O accumulator on most tiles.
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ u32x4 tr16_b64x2(const u16* p0, const u16* p1) {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -128,148 +164,225 @@ __device__ __forceinline__ u32x4 tr16_b64x2(const u16* p0, const u16* p1) {
     return u32x4{(unsigned)a, (unsigned)(a >> 32), (unsigned)b, (unsigned)(b >> 32)};
 }
 
-// One compute step over SUB = 64 keys of the LDS tile for the query blocks in
-// ACT (bit b set = block b has visible keys in this step).  `kl`/`vl` point at
-// the first key of the step inside the K / V tile; `key0` is that key's index
-// in the sequence.  Bit b of `need_mask` asks for element masking of block b
-// (diagonal tile or ragged key tail).
-template <bool BF16, int D, int QB, int NW, bool CAUSAL, unsigned ACT>
-__device__ __forceinline__ void attend_step(WaveState<D, QB>& st, const u16* kl, const u16* vl,
-                                            int lane, int key0, const int (&row0)[QB],
-                                            unsigned need_mask, int N, float scale_log2) {
-    using G = Geo<D, QB, NW>;
+// Per-lane LDS offsets (16-bit elements, relative to a tile) of the MFMA
+// operand fragments, swizzle included; fixed for the whole kernel.
+template <int D>
+struct FragOffsets {
+    int k[D / 16];        // K fragment of d step ks for key row (lane % 32); + 32*D for keys 32..63
+    int v[D / 32][2];     // V^T fragment halves of d block mt; + 16*D per 16-key group
+};
+
+template <class G>
+__device__ __forceinline__ FragOffsets<G::D> frag_offsets(int lane) {
+    constexpr int D = G::D;
+    FragOffsets<D> fo;
+    const int col = lane & 31, g = lane >> 5;
+    const int sw = chunk_swizzle<D>(col);
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) fo.k[ks] = col * D + (((2 * ks + g) ^ sw) << 3);
+    // ds_read_b64_tr_b16: each 16-lane group reads 4 key rows x 16 d; lane l
+    // supplies row tr_key (+8 for the second read), d = 32 mt + 16 dh + 4 (l % 4).
+    const int tr_key = 4 * g + ((lane >> 2) & 3);
+    const int dh = (lane >> 4) & 1;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int row = tr_key + 8 * r;
+            const int c = 4 * mt + 2 * dh + ((lane & 3) >> 1);
+            fo.v[mt][r] = row * D + ((c ^ chunk_swizzle<D>(row)) << 3) + 4 * (lane & 1);
+        }
+    return fo;
+}
+
+// S^T[key][query] = sum_d K[key][d] Q[query][d] for the 64 keys of one K
+// tile (two 32-key accumulators).  The 2*KS A-operand fragments stream
+// through a 4-deep register ring so each LDS read is issued four MFMAs ahead
+// of its use; consecutive MFMAs alternate between the two accumulators.
+template <bool BF16, class G>
+__device__ __forceinline__ void qk_tile(const WaveState<G::D>& st, const FragOffsets<G::D>& fo,
+                                        const u16* kt, f32x16 (&s)[2]) {
+    using M = Mma<BF16>;
+    constexpr int NF = 2 * G::KS;
+    auto kfrag = [&](int f) {
+        return *reinterpret_cast<const u32x4*>(kt + fo.k[f >> 1] + (f & 1) * 32 * G::D);
+    };
+    u32x4 ring[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) ring[f] = kfrag(f);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const u32x4 a = ring[f & 3];
+        if (f + 4 < NF) ring[f & 3] = kfrag(f + 4);
+        s[f & 1] = M::run(a, st.qf[f >> 1], s[f & 1]);
+    }
+}
+
+// Online-softmax update and O^T += V^T P^T for one 64-key tile whose raw
+// scores are in `s`.  Lane (col, g) holds keys 8(i/4) + 4g + i%4 of each
+// 32-key block for query row0 + col.  MASKED (diagonal tile or ragged key
+// tail) sets the scores of keys after the query or past N to -inf first.
+template <bool BF16, class G, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void softmax_pv_tile(WaveState<G::D>& st, const FragOffsets<G::D>& fo,
+                                                f32x16 (&s)[2], const u16* vt, int lane, int key0,
+                                                int row0, int N, float scale_log2) {
     using M = Mma<BF16>;
     const int g = lane >> 5;
     const int col = lane & 31;
 
-    // S^T[key][query] = sum_d K[key][d] Q[query][d] for two 32-key blocks.
-    f32x16 s[QB][2];
-#pragma unroll
-    for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[b][kb] = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const u16* kp = kl + (kb * 32 + col) * G::KP + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(kp + ks * 16);
-#pragma unroll
-            for (int b = 0; b < QB; ++b)
-                if (ACT & (1u << b)) s[b][kb] = M::run(a, st.qf[b][ks], s[b][kb]);
-        }
-    }
-
-    // Online softmax update per query block; P^T packed as the next B operand.
-    u32x4 pf[QB][4];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-        if (!(ACT & (1u << b))) continue;
-        if (need_mask & (1u << b)) {
-            const int qrow = row0[b] + col;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if ((CAUSAL && key > qrow) || key >= N) s[b][kb][i] = -INFINITY;
-                }
-        }
-        float mx = s[b][0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][kb][i]);
-        mx = fmaxf(mx, swap32_f32(mx));
-        const float m_new = fmaxf(st.m[b], mx * scale_log2);
-        const float alpha = online_rescale(st.m[b], m_new);
-        const float pivot = online_pivot(m_new);
-        float rs = 0.0f;
+    if constexpr (MASKED) {
+        // key0 + c + 4g is masked iff it is > row0 + col (causal) or >= N,
+        // i.e. iff the compile-time offset c exceeds lim.
+        const int lim = min(CAUSAL ? row0 + col - key0 : (1 << 30), N - 1 - key0) - 4 * g;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(fmaf(s[b][kb][i], scale_log2, -pivot));
-                s[b][kb][i] = p;
-                rs += p;
+                const int c = kb * 32 + 8 * (i >> 2) + (i & 3);
+                s[kb][i] = c > lim ? -INFINITY : s[kb][i];
             }
-        st.l[b] = st.l[b] * alpha + rs;
-        st.m[b] = m_new;
+    }
+    float mx = s[0][0];
 #pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) st.acc[b][mt] *= alpha;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int kb = u >> 1, h = (u & 1) * 8;
-            pf[b][u] = u32x4{M::pack(s[b][kb][h + 0], s[b][kb][h + 1]),
-                             M::pack(s[b][kb][h + 2], s[b][kb][h + 3]),
-                             M::pack(s[b][kb][h + 4], s[b][kb][h + 5]),
-                             M::pack(s[b][kb][h + 6], s[b][kb][h + 7])};
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = fmaxf(mx, swap32_f32(mx));
+    const float tile_m = mx * scale_log2;
+    // Each query decides for itself (so a row's result never depends on
+    // another row's data); the wave branches if any query needs to move, and
+    // the others multiply by exactly 1.
+    const bool grow = tile_m > st.m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? tile_m : st.m;
+        const float alpha = grow ? online_rescale(st.m, m_new) : 1.0f;
+        st.l *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) st.acc[mt] *= alpha;
+        st.m = m_new;
+    }
+
+    const float pivot = online_pivot(st.m);
+    u32x4 pf[4];
+    float rs0 = 0.0f, rs1 = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int kb = u >> 1, h = (u & 1) * 8;
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(s[kb][h + j], scale_log2, -pivot));
+        pf[u] = u32x4{M::pack(p[0], p[1]), M::pack(p[2], p[3]), M::pack(p[4], p[5]),
+                      M::pack(p[6], p[7])};
+        if constexpr (M::kSumRounded) {
+            rs0 = M::sum2(pf[u][0], rs0);
+            rs1 = M::sum2(pf[u][1], rs1);
+            rs0 = M::sum2(pf[u][2], rs0);
+            rs1 = M::sum2(pf[u][3], rs1);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                rs0 += p[j];
+                rs1 += p[j + 1];
+            }
         }
     }
+    st.l += rs0 + rs1;
 
     // O^T[d][query] += sum_key V^T[d][key] P^T[key][query].  B-operand slot
     // 8g+j of MFMA u holds key 16u + 8(j/4) + 4g + j%4 (the S^T accumulator
-    // order); the transpose reads fetch V^T in exactly that key order: each
-    // 16-lane group reads 4 key rows x 16 d, lane l ends with d = l%32.
-    const int tr_key = 4 * g + ((lane >> 2) & 3);
-    const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // order); the transpose reads fetch V^T in exactly that key order, lane l
+    // ending with d = 32 mt + l % 32.
+    constexpr int NV = 4 * G::MT;
+    auto vfrag = [&](int f) {
+        const u16* base = vt + (f / G::MT) * 16 * G::D;
+        return tr16_b64x2(base + fo.v[f % G::MT][0], base + fo.v[f % G::MT][1]);
+    };
+    u32x4 vring[4];
 #pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
+    for (int f = 0; f < 4; ++f) vring[f] = vfrag(f);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const u16* vp = vl + (u * 16 + tr_key) * G::VP + mt * 32 + tr_d;
-            const u32x4 a = tr16_b64x2(vp, vp + 8 * G::VP);
-#pragma unroll
-            for (int b = 0; b < QB; ++b)
-                if (ACT & (1u << b)) st.acc[b][mt] = M::run(a, pf[b][u], st.acc[b][mt]);
-        }
-}
-
-template <class G, int CPT>
-__device__ __forceinline__ void load_tile(u32x4 (&kr)[CPT], u32x4 (&vr)[CPT],
-                                          const u16* __restrict__ k, const u16* __restrict__ v,
-                                          int tile, int N, int tid) {
-    constexpr int D = G::D;
-#pragma unroll
-    for (int c = 0; c < G::CPT; ++c) {
-        const int id = tid + c * G::THREADS;
-        const int r = id / (D / 8), cc = id % (D / 8);
-        const int key = tile * G::BC + r;
-        if (key < N) {
-            const int64_t off = (int64_t)key * D + cc * 8;
-            kr[c] = *reinterpret_cast<const u32x4*>(k + off);
-            vr[c] = *reinterpret_cast<const u32x4*>(v + off);
-        } else {
-            kr[c] = u32x4{0u, 0u, 0u, 0u};
-            vr[c] = u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int f = 0; f < NV; ++f) {
+        const u32x4 a = vring[f & 3];
+        if (f + 4 < NV) vring[f & 3] = vfrag(f + 4);
+        st.acc[f % G::MT] = M::run(a, pf[f / G::MT], st.acc[f % G::MT]);
     }
 }
 
-template <class G, int CPT>
-__device__ __forceinline__ void store_tile(u16* stage, const u32x4 (&kr)[CPT],
-                                           const u32x4 (&vr)[CPT], int tid) {
+// Byte offset of an LDS location (what M0 and ds_* addresses use).
+__device__ __forceinline__ unsigned lds_offset(const void* p) {
+    return (unsigned)(unsigned long long)((const __attribute__((address_space(3))) char*)p);
+}
+
+// global_load_lds_dwordx4: each lane copies 16 bytes from gbase + voff to
+// LDS address m0 + 16 * lane.  Written as inline assembly so the compiler's
+// memory model does not see an LDS store: it would otherwise make every
+// later LDS read wait for the copy, which targets a stage that no wave reads
+// until the barrier after the matching wait_vmcnt.
+__device__ __forceinline__ void copy_to_lds16(const void* gbase, unsigned voff, void* lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_offset(lds_dst)), "v"(voff), "s"(gbase)
+                 : "m0");
+}
+
+// Issue the direct global->LDS copy of rows [tile*BC, tile*BC + BC) of one
+// head's K (or V) into an LDS tile.  Rows past N are clamped to row N-1: they
+// only feed keys that are masked (score -inf, weight exactly 0).
+template <class G>
+__device__ __forceinline__ void dma_tile(const u16* __restrict__ src, u16* dst, int tile, int N,
+                                         int w, int lane) {
     constexpr int D = G::D;
 #pragma unroll
-    for (int c = 0; c < G::CPT; ++c) {
-        const int id = tid + c * G::THREADS;
-        const int r = id / (D / 8), cc = id % (D / 8);
-        *reinterpret_cast<u32x4*>(stage + r * G::KP + cc * 8) = kr[c];
-        *reinterpret_cast<u32x4*>(stage + G::KT + r * G::VP + cc * 8) = vr[c];
+    for (int j = 0; j < G::BPW; ++j) {
+        const int blk = w * G::BPW + j;
+        const int r = blk * G::RPB + lane / G::CPR;
+        const int c = (lane % G::CPR) ^ chunk_swizzle<D>(r);
+        const int key = min(tile * G::BC + r, N - 1);
+        copy_to_lds16(src, (unsigned)((key * D + c * 8) * 2), dst + blk * 512);
     }
 }
 
-template <bool BF16, int D, bool CAUSAL, int QB, int NW>
-__global__ void __launch_bounds__(64 * NW)
+// Wait until at most `n` of this wave's vector-memory loads are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt low bits [3:0], expcnt and lgkmcnt left at
+// their maxima so they are not waited on).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | n);
+}
+
+// NW waves of 32 query rows; MINWG workgroups must fit on one CU at once
+// (this bounds the registers per wave).  Tile t lives in stage t % STAGES;
+// during iteration t the copy of tile t + DIST is in flight, and before the
+// iteration's one barrier each wave waits until its own part of tile t + 1
+// has landed.
+//
+// SPLIT (8 waves, two per SIMD): the hardware issues the older of the two
+// waves on a SIMD first, so if both run the same phase at the same time the
+// older one races through its tile and idles at the barrier while the
+// younger finishes alone.  Instead the second wave of each SIMD runs one
+// phase behind: waves 0-3 do QK(t), softmax(t), PV(t) in iteration t while
+// waves 4-7 do softmax(t-1), PV(t-1), QK(t), so one wave's MFMAs meet the
+// other's exponentials.  Waves 4-7 still read V(t-1) in iteration t, so the
+// copy in flight (tile t+2) must not reuse its stage: STAGES = DIST + 2.
+template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, bool SPLIT>
+__global__ void __launch_bounds__(64 * NW, MINWG)
 attn_fwd_kernel(const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
                 float* __restrict__ o, float* __restrict__ lse, int BH, int N, int T,
                 float scale_log2) {
-    using G = Geo<D, QB, NW>;
-    __shared__ __attribute__((aligned(16))) u16 lds[2 * G::STAGE];
+    using G = Geo<D, NW, STAGES, DIST>;
+    static_assert(STAGES >= DIST + (SPLIT ? 2 : 1), "a stage still being read would be overwritten");
+    __shared__ __attribute__((aligned(1024))) u16 lds[STAGES * G::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Waves w and w + NW/2 share a SIMD; with SPLIT they take adjacent
+    // 32-row blocks so their causal work is equal.
+    const bool lagging = SPLIT && w >= NW / 2;
+    const int block = SPLIT ? 2 * (w % (NW / 2)) + (lagging ? 1 : 0) : w;
 
     // Work item: longest causal tiles first; consecutive workgroups are
     // different heads of one query tile.
@@ -284,91 +397,140 @@ attn_fwd_kernel(const u16* __restrict__ q, const u16* __restrict__ k, const u16*
     lse += (int64_t)bh * N;
 
     const int row_base = t * G::BR;
-    int row0[QB];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) row0[b] = row_base + (b * G::NW + w) * 32;
+    const int row0 = row_base + block * 32;
     const int kv_end = CAUSAL ? min(row_base + G::BR, N) : N;
     const int ntiles = (kv_end + G::BC - 1) / G::BC;
+    // Tiles this wave attends to: 0 .. last_live (none if its rows are past N).
+    const int last_live = row0 >= N ? -1
+                        : min(ntiles - 1, CAUSAL ? (row0 + 31) / G::BC : ntiles - 1);
 
-    WaveState<D, QB> st;
+    WaveState<D> st;
     const int col = lane & 31, g = lane >> 5;
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-        const int row = row0[b] + col;
+    {
+        const int row = row0 + col;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
-            st.qf[b][ks] = row < N ? *reinterpret_cast<const u32x4*>(q + (int64_t)row * D + ks * 16 + 8 * g)
-                                   : u32x4{0u, 0u, 0u, 0u};
+            st.qf[ks] = row < N ? *reinterpret_cast<const u32x4*>(q + (int64_t)row * D + ks * 16 + 8 * g)
+                                : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) st.acc[b][mt] = f32x16{};
-        st.m[b] = -INFINITY;
-        st.l[b] = 0.0f;
+        for (int mt = 0; mt < G::MT; ++mt) st.acc[mt] = f32x16{};
+        st.m = -INFINITY;
+        st.l = 0.0f;
     }
+    const FragOffsets<D> fo = frag_offsets<G>(lane);
 
-    u32x4 kr[G::CPT], vr[G::CPT];
-    load_tile<G>(kr, vr, k, v, 0, N, tid);
-    store_tile<G>(lds, kr, vr, tid);
+    auto stage = [&](int it) { return lds + (it % STAGES) * G::STAGE; };
+    auto issue = [&](int it) {
+        if (it < ntiles) {
+            dma_tile<G>(k, stage(it), it, N, w, lane);
+            dma_tile<G>(v, stage(it) + G::TILE, it, N, w, lane);
+        }
+    };
+    // End of iteration `it`: tile it+1 complete for this wave (a copy issued
+    // later may stay in flight), then the barrier makes it complete for all.
+    auto finish = [&](int it) {
+        if constexpr (DIST == 2) {
+            if (it + 2 < ntiles)
+                wait_vmcnt<2 * G::BPW>();
+            else
+                wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+    };
+    auto qk = [&](int it, f32x16 (&s)[2]) { qk_tile<BF16, G>(st, fo, stage(it), s); };
+    // Finish tile `it`; a wave's diagonal or ragged-tail tile is its last
+    // live tile (rows start at multiples of 32, tiles hold 64 keys), so only
+    // that one can need masking.
+    auto smpv_last = [&](int it, f32x16 (&s)[2]) {
+        const int key0 = it * G::BC;
+        if ((CAUSAL && key0 + G::BC - 1 > row0) || key0 + G::BC > N)
+            softmax_pv_tile<BF16, G, CAUSAL, true>(st, fo, s, stage(it) + G::TILE, lane, key0, row0,
+                                                   N, scale_log2);
+        else
+            softmax_pv_tile<BF16, G, CAUSAL, false>(st, fo, s, stage(it) + G::TILE, lane, key0, row0,
+                                                    N, scale_log2);
+    };
+    auto smpv = [&](int it, f32x16 (&s)[2]) {
+        softmax_pv_tile<BF16, G, CAUSAL, false>(st, fo, s, stage(it) + G::TILE, lane, it * G::BC,
+                                                row0, N, scale_log2);
+    };
+
+    // Prologue: the first DIST tiles are copied while the Q fragments arrive;
+    // one full wait covers both (and tells the compiler Q is ready).
+#pragma unroll
+    for (int i = 0; i < DIST; ++i) issue(i);
+    wait_vmcnt<0>();
     __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
-        const bool more = it + 1 < ntiles;
-        if (more) load_tile<G>(kr, vr, k, v, it + 1, N, tid);
-        const u16* kl = lds + (it & 1) * G::STAGE;
-        const u16* vl = kl + G::KT;
-#pragma unroll
-        for (int sub = 0; sub < G::BC / G::SUB; ++sub) {
-            const int key0 = it * G::BC + sub * G::SUB;
-            unsigned act = 0, need = 0;
-#pragma unroll
-            for (int b = 0; b < QB; ++b) {
-                const bool live = row0[b] < N && key0 < N && (!CAUSAL || key0 <= row0[b] + 31);
-                const bool mask = (CAUSAL && key0 + G::SUB - 1 > row0[b]) || key0 + G::SUB > N;
-                act |= live ? (1u << b) : 0u;
-                need |= mask ? (1u << b) : 0u;
+    // All waves run all ntiles iterations (copies and barriers), whatever
+    // they compute; the loops are split so each holds one code variant.
+    f32x16 s[2];
+    int it = 0;
+    if (!lagging) {
+        for (; it < last_live; ++it) {
+            issue(it + DIST);
+            qk(it, s);
+            smpv(it, s);
+            finish(it);
+        }
+        if (it == last_live) {
+            issue(it + DIST);
+            qk(it, s);
+            smpv_last(it, s);
+            finish(it);
+            ++it;
+        }
+    } else {
+        if (last_live >= 0) {
+            issue(DIST);
+            qk(0, s);
+            finish(0);
+            it = 1;
+            for (; it <= last_live; ++it) {
+                issue(it + DIST);
+                smpv(it - 1, s);
+                qk(it, s);
+                finish(it);
             }
-            const u16* ks = kl + sub * G::SUB * G::KP;
-            const u16* vs = vl + sub * G::SUB * G::VP;
-            if constexpr (QB == 2) {
-                if (act == 3u)
-                    attend_step<BF16, D, QB, NW, CAUSAL, 3u>(st, ks, vs, lane, key0, row0, need, N, scale_log2);
-                else if (act == 2u)
-                    attend_step<BF16, D, QB, NW, CAUSAL, 2u>(st, ks, vs, lane, key0, row0, need, N, scale_log2);
-                else if (act == 1u)
-                    attend_step<BF16, D, QB, NW, CAUSAL, 1u>(st, ks, vs, lane, key0, row0, need, N, scale_log2);
+            if (it < ntiles) {
+                issue(it + DIST);
+                smpv_last(it - 1, s);
+                finish(it);
+                ++it;
             } else {
-                if (act == 1u)
-                    attend_step<BF16, D, QB, NW, CAUSAL, 1u>(st, ks, vs, lane, key0, row0, need, N, scale_log2);
+                smpv_last(it - 1, s);  // no copy or barrier left to keep in step with
             }
         }
-        if (more) store_tile<G>(lds + ((it + 1) & 1) * G::STAGE, kr, vr, tid);
-        __syncthreads();
+    }
+    for (; it < ntiles; ++it) {
+        issue(it + DIST);
+        finish(it);
     }
 
     // Epilogue: combine the two lane halves of each query, normalise, store.
+    const float l_tot = st.l + swap32_f32(st.l);
+    const int row = row0 + col;
+    if (row < N) {
+        const float inv = 1.0f / l_tot;
+        float* orow = o + (int64_t)row * D;
 #pragma unroll
-    for (int b = 0; b < QB; ++b) {
-        const float l_tot = st.l[b] + swap32_f32(st.l[b]);
-        const int row = row0[b] + col;
-        if (row < N) {
-            const float inv = 1.0f / l_tot;
-            float* orow = o + (int64_t)row * D;
+        for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x4 r = {st.acc[b][mt][4 * i4 + 0] * inv, st.acc[b][mt][4 * i4 + 1] * inv,
-                                     st.acc[b][mt][4 * i4 + 2] * inv, st.acc[b][mt][4 * i4 + 3] * inv};
-                    *reinterpret_cast<f32x4*>(orow + mt * 32 + 8 * i4 + 4 * g) = r;
-                }
-            if (g == 0) lse[row] = (st.m[b] + log2f(l_tot)) * kLn2;
-        }
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 r = {st.acc[mt][4 * i4 + 0] * inv, st.acc[mt][4 * i4 + 1] * inv,
+                                 st.acc[mt][4 * i4 + 2] * inv, st.acc[mt][4 * i4 + 3] * inv};
+                *reinterpret_cast<f32x4*>(orow + mt * 32 + 8 * i4 + 4 * g) = r;
+            }
+        if (g == 0) lse[row] = (st.m + log2f(l_tot)) * kLn2;
     }
 }
 
-template <bool BF16, int D, bool CAUSAL, int QB, int NW>
+template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, bool SPLIT>
 hipError_t launch_one(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
                       int N, hipStream_t stream) {
-    using G = Geo<D, QB, NW>;
+    using G = Geo<D, NW, STAGES, DIST>;
     const int T = (N + G::BR - 1) / G::BR;
     const float scale_log2 = kLog2e / __builtin_sqrtf((float)D);
     const u16* qq = static_cast<const u16*>(q);
@@ -376,40 +538,50 @@ hipError_t launch_one(const void* q, const void* k, const void* v, float* o, flo
     const u16* vv = static_cast<const u16*>(v);
     void* args[] = {(void*)&qq, (void*)&kk, (void*)&vv, (void*)&o, (void*)&lse,
                     (void*)&BH, (void*)&N, (void*)const_cast<int*>(&T), (void*)const_cast<float*>(&scale_log2)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, QB, NW>),
-                           dim3((unsigned)(T * BH)), dim3(G::THREADS), args, 0, stream);
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, NW, MINWG, STAGES, DIST, SPLIT>),
+        dim3((unsigned)(T * BH)), dim3(G::THREADS), args, 0, stream);
 }
 
+// 8 waves, one workgroup per CU, phase-split, copies two tiles ahead (four
+// stages); or 4 waves, two independent workgroups per CU (LDS for two: copies
+// one tile ahead at D = 128, two at D = 64).
 template <bool BF16, int D, bool CAUSAL>
-hipError_t launch_qb(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
-                     int N, int qb, hipStream_t stream) {
-    return qb == 1 ? launch_one<BF16, D, CAUSAL, 1, 4>(q, k, v, o, lse, BH, N, stream)
-                   : launch_one<BF16, D, CAUSAL, 1, 8>(q, k, v, o, lse, BH, N, stream);
+hipError_t launch_cfg(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
+                      int N, int waves, hipStream_t stream) {
+    if (waves == 4) {
+        if constexpr (D == 128)
+            return launch_one<BF16, D, CAUSAL, 4, 2, 2, 1, false>(q, k, v, o, lse, BH, N, stream);
+        else
+            return launch_one<BF16, D, CAUSAL, 4, 2, 3, 2, false>(q, k, v, o, lse, BH, N, stream);
+    }
+    return launch_one<BF16, D, CAUSAL, 8, 1, 4, 2, true>(q, k, v, o, lse, BH, N, stream);
 }
 
 }  // namespace
 
-// Rows per workgroup: 256 (two 32-row blocks per wave) when that still gives
-// at least one workgroup per CU, else 128.
-int attn_pick_qb(int64_t BH, int64_t N) {
+// Waves per workgroup: 8 (256 query rows, one workgroup per CU, each K/V
+// tile read serves 256 rows) when that still gives at least two workgroups
+// per CU; else 4 (128 rows, two workgroups per CU) for more parallelism.
+int attn_pick_waves(int64_t BH, int64_t N) {
     const int64_t wgs_big = BH * ((N + 255) / 256);
-    return wgs_big >= 256 ? 2 : 1;
+    return wgs_big >= 512 ? 8 : 4;
 }
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
-                           int BH, int N, int D, bool causal, bool bf16, int qb, hipStream_t stream) {
+                           int BH, int N, int D, bool causal, bool bf16, int waves, hipStream_t stream) {
     if (D == 128) {
         if (bf16)
-            return causal ? launch_qb<true, 128, true>(q, k, v, o, lse, BH, N, qb, stream)
-                          : launch_qb<true, 128, false>(q, k, v, o, lse, BH, N, qb, stream);
-        return causal ? launch_qb<false, 128, true>(q, k, v, o, lse, BH, N, qb, stream)
-                      : launch_qb<false, 128, false>(q, k, v, o, lse, BH, N, qb, stream);
+            return causal ? launch_cfg<true, 128, true>(q, k, v, o, lse, BH, N, waves, stream)
+                          : launch_cfg<true, 128, false>(q, k, v, o, lse, BH, N, waves, stream);
+        return causal ? launch_cfg<false, 128, true>(q, k, v, o, lse, BH, N, waves, stream)
+                      : launch_cfg<false, 128, false>(q, k, v, o, lse, BH, N, waves, stream);
     }
     if (bf16)
-        return causal ? launch_qb<true, 64, true>(q, k, v, o, lse, BH, N, qb, stream)
-                      : launch_qb<true, 64, false>(q, k, v, o, lse, BH, N, qb, stream);
-    return causal ? launch_qb<false, 64, true>(q, k, v, o, lse, BH, N, qb, stream)
-                  : launch_qb<false, 64, false>(q, k, v, o, lse, BH, N, qb, stream);
+        return causal ? launch_cfg<true, 64, true>(q, k, v, o, lse, BH, N, waves, stream)
+                      : launch_cfg<true, 64, false>(q, k, v, o, lse, BH, N, waves, stream);
+    return causal ? launch_cfg<false, 64, true>(q, k, v, o, lse, BH, N, waves, stream)
+                  : launch_cfg<false, 64, false>(q, k, v, o, lse, BH, N, waves, stream);
 }
 
 }  // namespace osc
