@@ -91,6 +91,27 @@ attn_status_t attn_fwd(const void *q, const void *k, const void *v, float *o, fl
                        attn_dtype_t dtype, hipStream_t stream);
 
 /*
+ * attn_fwd_gqa - attention forward with grouped key/value heads
+ * (grouped-query / multi-query attention).
+ *
+ * Query head h of batch b attends with K/V head floor(h / (H / Hkv)) of the
+ * same batch, without the K/V heads being copied ("CUDA KV Cache: paged
+ * storage and long-context decode" (chengzipai.xyz), section 3: the query
+ * head maps to the shared KV head as h_kv = floor(h_q / g); FA page,
+ * section 7).  Hkv = H is attn_fwd; Hkv = 1 is multi-query attention.
+ *
+ *   q        [B, H, N, D] of `dtype`, 16-byte aligned.
+ *   k, v     [B, Hkv, N, D] of `dtype`, 16-byte aligned.
+ *   o, lse   as for attn_fwd ([B, H, N, D] and [B, H, N], FP32).
+ *   Hkv      number of key/value heads: 1 <= Hkv <= H and H % Hkv == 0,
+ *            else ATTN_ERR_SHAPE.
+ * Everything else (D, dtype, causal, limits, errors, stream) is as for attn_fwd.
+ */
+attn_status_t attn_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse,
+                           int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal,
+                           attn_dtype_t dtype, hipStream_t stream);
+
+/*
  * row_softmax - y[r, :] = softmax(x[r, :]) for r < M.
  *
  *   x   [M, N] FP32 input, row-major, 4-byte aligned (rows need not be

@@ -9,6 +9,7 @@ The entry points mirror the C ABI in ``include/osc_attn.h``:
 
     attn_fwd(q, k, v, o, lse, B, H, N, D, causal, dtype, stream=None)
     row_softmax(x, y, M, N, stream=None)
+    attn_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, stream=None)
     attn_status_str(status)
 
 Pointer arguments accept device tensors (``torch.Tensor``, only its address is
@@ -36,7 +37,7 @@ STATUS = {
     5: "ATTN_ERR_LAUNCH",
     6: "ATTN_ERR_ALIAS",
 }
-EXPORTS = ("attn_fwd", "row_softmax", "attn_status_str")
+EXPORTS = ("attn_fwd", "attn_fwd_gqa", "row_softmax", "attn_status_str")
 
 _lib = None
 
@@ -60,6 +61,9 @@ def load():
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                 ctypes.c_int, vp]
+    lib.attn_fwd_gqa.restype = ctypes.c_int
     lib.row_softmax.argtypes = [vp, vp, i64, i64, vp]
     lib.row_softmax.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
@@ -109,6 +113,15 @@ def attn_fwd(q, k, v, o, lse, B, H, N, D, causal, dtype, stream=None) -> None:
                          int(D), int(bool(causal)), _dtype(dtype), _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_fwd")
+
+
+def attn_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, stream=None) -> None:
+    """Enqueue grouped-query attention forward (K/V have Hkv heads, Hkv divides H)."""
+    st = load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                             int(Hkv), int(N), int(D), int(bool(causal)), _dtype(dtype),
+                             _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_gqa")
 
 
 def row_softmax(x, y, M, N, stream=None) -> None:

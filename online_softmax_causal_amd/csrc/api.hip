@@ -8,16 +8,27 @@
 
 extern "C" {
 
+static attn_status_t attn_fwd_impl(const void* q, const void* k, const void* v, float* o,
+                                   float* lse, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                                   int64_t D, int causal, attn_dtype_t dtype, hipStream_t stream) {
+    const attn_status_t st = osc::validate_attn(q, k, v, o, lse, B, H, Hkv, N, D, dtype);
+    if (st != ATTN_OK) return st;
+    const int waves = osc::attn_pick_waves(B * H, N);
+    const hipError_t e = osc::launch_attn_fwd(q, k, v, o, lse, (int)B, (int)H, (int)Hkv, (int)N,
+                                              (int)D, causal != 0, dtype == ATTN_BF16, waves, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
                        int64_t B, int64_t H, int64_t N, int64_t D, int causal,
                        attn_dtype_t dtype, hipStream_t stream) {
-    const attn_status_t st = osc::validate_attn(q, k, v, o, lse, B, H, N, D, dtype);
-    if (st != ATTN_OK) return st;
-    const int64_t BH = B * H;
-    const int waves = osc::attn_pick_waves(BH, N);
-    const hipError_t e = osc::launch_attn_fwd(q, k, v, o, lse, (int)BH, (int)N, (int)D,
-                                              causal != 0, dtype == ATTN_BF16, waves, stream);
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    return attn_fwd_impl(q, k, v, o, lse, B, H, H, N, D, causal, dtype, stream);
+}
+
+attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, float* o, float* lse,
+                           int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal,
+                           attn_dtype_t dtype, hipStream_t stream) {
+    return attn_fwd_impl(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, stream);
 }
 
 attn_status_t row_softmax(const float* x, float* y, int64_t M, int64_t N, hipStream_t stream) {

@@ -112,14 +112,14 @@ struct Mma<true> {
 // consecutive rows read by one ds_read_b128 phase 16 distinct 16-byte bank
 // groups, and the 4 rows x 4 chunks of one 32-lane ds_read_b64_tr_b16 phase
 // 16 distinct bank groups as well.
-template <int D_, int NW_, int STAGES_, int DIST_>
+template <int D_, int NW_, int STAGES_, int DIST_, int DMAW_>
 struct Geo {
     static constexpr int D = D_;
-    static constexpr int NW = NW_;              // waves per workgroup, 32 query rows each
+    static constexpr int NW = NW_;              // waves per workgroup
+    static constexpr int DMAW = DMAW_;          // waves that issue the tile copies
     static constexpr int STAGES = STAGES_;      // LDS stages
     static constexpr int DIST = DIST_;          // tiles copied ahead of the one being computed
     static constexpr int THREADS = 64 * NW;
-    static constexpr int BR = 32 * NW;          // query rows per workgroup
     static constexpr int BC = 64;               // keys per tile
     static constexpr int MT = D / 32;           // 32-row d blocks of O^T
     static constexpr int KS = D / 16;           // 16-wide d steps of Q K^T
@@ -127,8 +127,8 @@ struct Geo {
     static constexpr int RPB = 1024 / (2 * D);  // rows per 1 KiB block
     static constexpr int TILE = BC * D;         // 16-bit elements per K (or V) tile
     static constexpr int STAGE = 2 * TILE;
-    static constexpr int BPW = BC / RPB / NW;   // 1 KiB blocks per wave per tile
-    static_assert(BPW >= 1 && BPW * RPB * NW == BC, "tile fill must divide evenly");
+    static constexpr int BPW = BC / RPB / DMAW; // 1 KiB blocks per copying wave per tile
+    static_assert(BPW >= 1 && BPW * RPB * DMAW == BC, "tile fill must divide evenly");
     static_assert(DIST == 1 || DIST == 2, "prefetch distance");
 };
 
@@ -140,12 +140,27 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
         return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <int D>
+// Kernel arguments (one struct, passed by value).
+struct AttnArgs {
+    const u16* q;   // [B, H, N, D]
+    const u16* k;   // [B, Hkv, N, D]
+    const u16* v;   // [B, Hkv, N, D]
+    float* o;       // [B, H, N, D]
+    float* lse;     // [B, H, N]
+    int BH;         // B * H
+    int H;          // query heads
+    int Hkv;        // key/value heads (divides H)
+    int N;          // sequence length
+    int T;          // query tiles per head
+    float scale_log2;  // log2(e) / sqrt(D)
+};
+
+template <int D, int QB>
 struct WaveState {
-    u32x4 qf[D / 16];     // Q^T fragments (MFMA B operand), one per 16-wide d step
-    f32x16 acc[D / 32];   // O^T accumulators, 32 d-rows each
-    float m;              // reference max of this lane's query, log2 units
-    float l;              // this lane's share of the running sum (relative to m)
+    u32x4 qf[QB][D / 16];     // Q^T fragments (MFMA B operand), one per 16-wide d step
+    f32x16 acc[QB][D / 32];   // O^T accumulators, 32 d-rows each
+    float m[QB];              // reference max of this lane's query, log2 units
+    float l[QB];              // this lane's share of the running sum (relative to m)
 };
 
 // Conditional rescaling: the reference max m moves only when a query's
@@ -196,12 +211,13 @@ __device__ __forceinline__ FragOffsets<G::D> frag_offsets(int lane) {
 }
 
 // S^T[key][query] = sum_d K[key][d] Q[query][d] for the 64 keys of one K
-// tile (two 32-key accumulators).  The 2*KS A-operand fragments stream
-// through a 4-deep register ring so each LDS read is issued four MFMAs ahead
-// of its use; consecutive MFMAs alternate between the two accumulators.
-template <bool BF16, class G>
-__device__ __forceinline__ void qk_tile(const WaveState<G::D>& st, const FragOffsets<G::D>& fo,
-                                        const u16* kt, f32x16 (&s)[2]) {
+// tile (two 32-key accumulators per query block).  The 2*KS A-operand
+// fragments stream through a 4-deep register ring so each LDS read is issued
+// four fragments ahead of its use; each fragment feeds the MFMAs of all QB
+// query blocks, and consecutive MFMAs alternate accumulators.
+template <bool BF16, class G, int QB>
+__device__ __forceinline__ void qk_tile(const WaveState<G::D, QB>& st, const FragOffsets<G::D>& fo,
+                                        const u16* kt, f32x16 (&s)[QB][2]) {
     using M = Mma<BF16>;
     constexpr int NF = 2 * G::KS;
     auto kfrag = [&](int f) {
@@ -210,90 +226,112 @@ __device__ __forceinline__ void qk_tile(const WaveState<G::D>& st, const FragOff
     u32x4 ring[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) ring[f] = kfrag(f);
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        s[b][0] = f32x16{};
+        s[b][1] = f32x16{};
+    }
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         const u32x4 a = ring[f & 3];
         if (f + 4 < NF) ring[f & 3] = kfrag(f + 4);
-        s[f & 1] = M::run(a, st.qf[f >> 1], s[f & 1]);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) s[b][f & 1] = M::run(a, st.qf[b][f >> 1], s[b][f & 1]);
     }
 }
 
 // Online-softmax update and O^T += V^T P^T for one 64-key tile whose raw
 // scores are in `s`.  Lane (col, g) holds keys 8(i/4) + 4g + i%4 of each
-// 32-key block for query row0 + col.  MASKED (diagonal tile or ragged key
-// tail) sets the scores of keys after the query or past N to -inf first.
-template <bool BF16, class G, bool CAUSAL, bool MASKED>
-__device__ __forceinline__ void softmax_pv_tile(WaveState<G::D>& st, const FragOffsets<G::D>& fo,
-                                                f32x16 (&s)[2], const u16* vt, int lane, int key0,
-                                                int row0, int N, float scale_log2) {
+// 32-key block for query row0[b] + col of query block b.  MASKED (diagonal
+// tile or ragged key tail) sets the scores of keys after the query or past N
+// to -inf first.
+template <bool BF16, class G, bool CAUSAL, bool MASKED, int QB>
+__device__ __forceinline__ void softmax_pv_tile(WaveState<G::D, QB>& st, const FragOffsets<G::D>& fo,
+                                                f32x16 (&s)[QB][2], const u16* vt, int lane,
+                                                int key0, const int (&row0)[QB], int N,
+                                                float scale_log2) {
     using M = Mma<BF16>;
     const int g = lane >> 5;
     const int col = lane & 31;
 
     if constexpr (MASKED) {
-        // key0 + c + 4g is masked iff it is > row0 + col (causal) or >= N,
-        // i.e. iff the compile-time offset c exceeds lim.
-        const int lim = min(CAUSAL ? row0 + col - key0 : (1 << 30), N - 1 - key0) - 4 * g;
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            // key0 + c + 4g is masked iff it is > row0 + col (causal) or >= N,
+            // i.e. iff the compile-time offset c exceeds lim.
+            const int lim = min(CAUSAL ? row0[b] + col - key0 : (1 << 30), N - 1 - key0) - 4 * g;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int c = kb * 32 + 8 * (i >> 2) + (i & 3);
+                    s[b][kb][i] = c > lim ? -INFINITY : s[b][kb][i];
+                }
+        }
+    }
+    float tile_m[QB];
+    bool grow[QB];
+    bool any_grow = false;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        float mx = s[b][0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int c = kb * 32 + 8 * (i >> 2) + (i & 3);
-                s[kb][i] = c > lim ? -INFINITY : s[kb][i];
-            }
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][kb][i]);
+        mx = fmaxf(mx, swap32_f32(mx));
+        tile_m[b] = mx * scale_log2;
+        grow[b] = tile_m[b] > st.m[b] + kRescaleSlack;
+        any_grow = any_grow || grow[b];
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, swap32_f32(mx));
-    const float tile_m = mx * scale_log2;
     // Each query decides for itself (so a row's result never depends on
     // another row's data); the wave branches if any query needs to move, and
     // the others multiply by exactly 1.
-    const bool grow = tile_m > st.m + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? tile_m : st.m;
-        const float alpha = grow ? online_rescale(st.m, m_new) : 1.0f;
-        st.l *= alpha;
+    if (__builtin_amdgcn_ballot_w64(any_grow) != 0) {
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) st.acc[mt] *= alpha;
-        st.m = m_new;
-    }
-
-    const float pivot = online_pivot(st.m);
-    u32x4 pf[4];
-    float rs0 = 0.0f, rs1 = 0.0f;
+        for (int b = 0; b < QB; ++b) {
+            const float m_new = grow[b] ? tile_m[b] : st.m[b];
+            const float alpha = grow[b] ? online_rescale(st.m[b], m_new) : 1.0f;
+            st.l[b] *= alpha;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int kb = u >> 1, h = (u & 1) * 8;
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(s[kb][h + j], scale_log2, -pivot));
-        pf[u] = u32x4{M::pack(p[0], p[1]), M::pack(p[2], p[3]), M::pack(p[4], p[5]),
-                      M::pack(p[6], p[7])};
-        if constexpr (M::kSumRounded) {
-            rs0 = M::sum2(pf[u][0], rs0);
-            rs1 = M::sum2(pf[u][1], rs1);
-            rs0 = M::sum2(pf[u][2], rs0);
-            rs1 = M::sum2(pf[u][3], rs1);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-                rs0 += p[j];
-                rs1 += p[j + 1];
-            }
+            for (int mt = 0; mt < G::MT; ++mt) st.acc[b][mt] *= alpha;
+            st.m[b] = m_new;
         }
     }
-    st.l += rs0 + rs1;
+
+    u32x4 pf[QB][4];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const float pivot = online_pivot(st.m[b]);
+        float rs0 = 0.0f, rs1 = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kb = u >> 1, h = (u & 1) * 8;
+            float p[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(s[b][kb][h + j], scale_log2, -pivot));
+            pf[b][u] = u32x4{M::pack(p[0], p[1]), M::pack(p[2], p[3]), M::pack(p[4], p[5]),
+                             M::pack(p[6], p[7])};
+            if constexpr (M::kSumRounded) {
+                rs0 = M::sum2(pf[b][u][0], rs0);
+                rs1 = M::sum2(pf[b][u][1], rs1);
+                rs0 = M::sum2(pf[b][u][2], rs0);
+                rs1 = M::sum2(pf[b][u][3], rs1);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    rs0 += p[j];
+                    rs1 += p[j + 1];
+                }
+            }
+        }
+        st.l[b] += rs0 + rs1;
+    }
 
     // O^T[d][query] += sum_key V^T[d][key] P^T[key][query].  B-operand slot
     // 8g+j of MFMA u holds key 16u + 8(j/4) + 4g + j%4 (the S^T accumulator
     // order); the transpose reads fetch V^T in exactly that key order, lane l
-    // ending with d = 32 mt + l % 32.
+    // ending with d = 32 mt + l % 32.  Each fragment feeds all query blocks.
     constexpr int NV = 4 * G::MT;
     auto vfrag = [&](int f) {
         const u16* base = vt + (f / G::MT) * 16 * G::D;
@@ -306,7 +344,9 @@ __device__ __forceinline__ void softmax_pv_tile(WaveState<G::D>& st, const FragO
     for (int f = 0; f < NV; ++f) {
         const u32x4 a = vring[f & 3];
         if (f + 4 < NV) vring[f & 3] = vfrag(f + 4);
-        st.acc[f % G::MT] = M::run(a, pf[f / G::MT], st.acc[f % G::MT]);
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+            st.acc[b][f % G::MT] = M::run(a, pf[b][f / G::MT], st.acc[b][f % G::MT]);
     }
 }
 
@@ -367,13 +407,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // waves 4-7 do softmax(t-1), PV(t-1), QK(t), so one wave's MFMAs meet the
 // other's exponentials.  Waves 4-7 still read V(t-1) in iteration t, so the
 // copy in flight (tile t+2) must not reuse its stage: STAGES = DIST + 2.
-template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, bool SPLIT>
+// The tile copies are issued by waves 0-3 only: the lagging waves are on the
+// critical path of every iteration.
+template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, bool SPLIT, int QB>
 __global__ void __launch_bounds__(64 * NW, MINWG)
-attn_fwd_kernel(const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-                float* __restrict__ o, float* __restrict__ lse, int BH, int N, int T,
-                float scale_log2) {
-    using G = Geo<D, NW, STAGES, DIST>;
+attn_fwd_kernel(AttnArgs args) {
+    using G = Geo<D, NW, STAGES, DIST, SPLIT ? NW / 2 : NW>;
     static_assert(STAGES >= DIST + (SPLIT ? 2 : 1), "a stage still being read would be overwritten");
+    static_assert(!SPLIT || QB == 1, "the phase split pairs single-block waves");
+    constexpr int BR = 32 * QB * NW;   // query rows per workgroup
     __shared__ __attribute__((aligned(1024))) u16 lds[STAGES * G::STAGE];
 
     const int tid = threadIdx.x;
@@ -384,44 +426,58 @@ attn_fwd_kernel(const u16* __restrict__ q, const u16* __restrict__ k, const u16*
     const bool lagging = SPLIT && w >= NW / 2;
     const int block = SPLIT ? 2 * (w % (NW / 2)) + (lagging ? 1 : 0) : w;
 
+    const int N = args.N;
+    const float scale_log2 = args.scale_log2;
     // Work item: longest causal tiles first; consecutive workgroups are
-    // different heads of one query tile.
+    // different heads of one query tile.  Workgroups are dealt round-robin
+    // to the 8 XCDs (workgroup i to XCD i % 8), each with its own L2.  When
+    // BH is a multiple of 8, XCD x takes the contiguous heads
+    // [x BH/8, (x+1) BH/8) of every query tile, so all query tiles of a head,
+    // and the query heads that share a K/V head, meet in one L2.
     const int bid = blockIdx.x;
-    const int t = CAUSAL ? (T - 1 - bid / BH) : (bid / BH);
-    const int bh = bid % BH;
-    const int64_t head = (int64_t)bh * N * D;
-    q += head;
-    k += head;
-    v += head;
-    o += head;
-    lse += (int64_t)bh * N;
+    const int t = CAUSAL ? (args.T - 1 - bid / args.BH) : (bid / args.BH);
+    const int j = bid % args.BH;
+    const int bh = (args.BH & 7) ? j : (j & 7) * (args.BH >> 3) + (j >> 3);
+    // Query head h of batch b reads K/V head h / (H / Hkv) of the same batch
+    // (grouped-query attention; Hkv = H is ordinary multi-head attention).
+    const int kvh = (bh / args.H) * args.Hkv + (bh % args.H) / (args.H / args.Hkv);
+    const u16* __restrict__ q = args.q + (int64_t)bh * N * D;
+    const u16* __restrict__ k = args.k + (int64_t)kvh * N * D;
+    const u16* __restrict__ v = args.v + (int64_t)kvh * N * D;
+    float* __restrict__ o = args.o + (int64_t)bh * N * D;
+    float* __restrict__ lse = args.lse + (int64_t)bh * N;
 
-    const int row_base = t * G::BR;
-    const int row0 = row_base + block * 32;
-    const int kv_end = CAUSAL ? min(row_base + G::BR, N) : N;
+    const int row_base = t * BR;
+    // Query block b of this wave starts at row0[b]; with QB = 2 the two
+    // blocks are adjacent and share their diagonal 64-key tile.
+    int row0[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) row0[b] = row_base + (QB * block + b) * 32;
+    const int kv_end = CAUSAL ? min(row_base + BR, N) : N;
     const int ntiles = (kv_end + G::BC - 1) / G::BC;
     // Tiles this wave attends to: 0 .. last_live (none if its rows are past N).
-    const int last_live = row0 >= N ? -1
-                        : min(ntiles - 1, CAUSAL ? (row0 + 31) / G::BC : ntiles - 1);
+    const int last_live = row0[0] >= N ? -1
+                        : min(ntiles - 1, CAUSAL ? (row0[QB - 1] + 31) / G::BC : ntiles - 1);
 
-    WaveState<D> st;
+    WaveState<D, QB> st;
     const int col = lane & 31, g = lane >> 5;
-    {
-        const int row = row0 + col;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const int row = row0[b] + col;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
-            st.qf[ks] = row < N ? *reinterpret_cast<const u32x4*>(q + (int64_t)row * D + ks * 16 + 8 * g)
-                                : u32x4{0u, 0u, 0u, 0u};
+            st.qf[b][ks] = row < N ? *reinterpret_cast<const u32x4*>(q + (int64_t)row * D + ks * 16 + 8 * g)
+                                   : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) st.acc[mt] = f32x16{};
-        st.m = -INFINITY;
-        st.l = 0.0f;
+        for (int mt = 0; mt < G::MT; ++mt) st.acc[b][mt] = f32x16{};
+        st.m[b] = -INFINITY;
+        st.l[b] = 0.0f;
     }
     const FragOffsets<D> fo = frag_offsets<G>(lane);
 
     auto stage = [&](int it) { return lds + (it % STAGES) * G::STAGE; };
     auto issue = [&](int it) {
-        if (it < ntiles) {
+        if (it < ntiles && w < G::DMAW) {
             dma_tile<G>(k, stage(it), it, N, w, lane);
             dma_tile<G>(v, stage(it) + G::TILE, it, N, w, lane);
         }
@@ -439,22 +495,23 @@ attn_fwd_kernel(const u16* __restrict__ q, const u16* __restrict__ k, const u16*
         }
         __syncthreads();
     };
-    auto qk = [&](int it, f32x16 (&s)[2]) { qk_tile<BF16, G>(st, fo, stage(it), s); };
+    auto qk = [&](int it, f32x16 (&s)[QB][2]) { qk_tile<BF16, G, QB>(st, fo, stage(it), s); };
     // Finish tile `it`; a wave's diagonal or ragged-tail tile is its last
-    // live tile (rows start at multiples of 32, tiles hold 64 keys), so only
-    // that one can need masking.
-    auto smpv_last = [&](int it, f32x16 (&s)[2]) {
+    // live tile (blocks start at multiples of 32 rows and a wave's blocks lie
+    // in one 64-row span, tiles hold 64 keys), so only that one can need
+    // masking.
+    auto smpv_last = [&](int it, f32x16 (&s)[QB][2]) {
         const int key0 = it * G::BC;
-        if ((CAUSAL && key0 + G::BC - 1 > row0) || key0 + G::BC > N)
-            softmax_pv_tile<BF16, G, CAUSAL, true>(st, fo, s, stage(it) + G::TILE, lane, key0, row0,
-                                                   N, scale_log2);
+        if ((CAUSAL && key0 + G::BC - 1 > row0[0]) || key0 + G::BC > N)
+            softmax_pv_tile<BF16, G, CAUSAL, true, QB>(st, fo, s, stage(it) + G::TILE, lane, key0,
+                                                       row0, N, scale_log2);
         else
-            softmax_pv_tile<BF16, G, CAUSAL, false>(st, fo, s, stage(it) + G::TILE, lane, key0, row0,
-                                                    N, scale_log2);
+            softmax_pv_tile<BF16, G, CAUSAL, false, QB>(st, fo, s, stage(it) + G::TILE, lane, key0,
+                                                        row0, N, scale_log2);
     };
-    auto smpv = [&](int it, f32x16 (&s)[2]) {
-        softmax_pv_tile<BF16, G, CAUSAL, false>(st, fo, s, stage(it) + G::TILE, lane, it * G::BC,
-                                                row0, N, scale_log2);
+    auto smpv = [&](int it, f32x16 (&s)[QB][2]) {
+        softmax_pv_tile<BF16, G, CAUSAL, false, QB>(st, fo, s, stage(it) + G::TILE, lane, it * G::BC,
+                                                    row0, N, scale_log2);
     };
 
     // Prologue: the first DIST tiles are copied while the Q fragments arrive;
@@ -466,7 +523,7 @@ attn_fwd_kernel(const u16* __restrict__ q, const u16* __restrict__ k, const u16*
 
     // All waves run all ntiles iterations (copies and barriers), whatever
     // they compute; the loops are split so each holds one code variant.
-    f32x16 s[2];
+    f32x16 s[QB][2];
     int it = 0;
     if (!lagging) {
         for (; it < last_live; ++it) {
@@ -510,52 +567,50 @@ attn_fwd_kernel(const u16* __restrict__ q, const u16* __restrict__ k, const u16*
     }
 
     // Epilogue: combine the two lane halves of each query, normalise, store.
-    const float l_tot = st.l + swap32_f32(st.l);
-    const int row = row0 + col;
-    if (row < N) {
-        const float inv = 1.0f / l_tot;
-        float* orow = o + (int64_t)row * D;
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt)
+    for (int b = 0; b < QB; ++b) {
+        const float l_tot = st.l[b] + swap32_f32(st.l[b]);
+        const int row = row0[b] + col;
+        if (row < N) {
+            const float inv = 1.0f / l_tot;
+            float* orow = o + (int64_t)row * D;
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 r = {st.acc[mt][4 * i4 + 0] * inv, st.acc[mt][4 * i4 + 1] * inv,
-                                 st.acc[mt][4 * i4 + 2] * inv, st.acc[mt][4 * i4 + 3] * inv};
-                *reinterpret_cast<f32x4*>(orow + mt * 32 + 8 * i4 + 4 * g) = r;
-            }
-        if (g == 0) lse[row] = (st.m + log2f(l_tot)) * kLn2;
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 r = {st.acc[b][mt][4 * i4 + 0] * inv, st.acc[b][mt][4 * i4 + 1] * inv,
+                                     st.acc[b][mt][4 * i4 + 2] * inv, st.acc[b][mt][4 * i4 + 3] * inv};
+                    *reinterpret_cast<f32x4*>(orow + mt * 32 + 8 * i4 + 4 * g) = r;
+                }
+            if (g == 0) lse[row] = (st.m[b] + log2f(l_tot)) * kLn2;
+        }
     }
 }
 
-template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, bool SPLIT>
-hipError_t launch_one(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
-                      int N, hipStream_t stream) {
-    using G = Geo<D, NW, STAGES, DIST>;
-    const int T = (N + G::BR - 1) / G::BR;
-    const float scale_log2 = kLog2e / __builtin_sqrtf((float)D);
-    const u16* qq = static_cast<const u16*>(q);
-    const u16* kk = static_cast<const u16*>(k);
-    const u16* vv = static_cast<const u16*>(v);
-    void* args[] = {(void*)&qq, (void*)&kk, (void*)&vv, (void*)&o, (void*)&lse,
-                    (void*)&BH, (void*)&N, (void*)const_cast<int*>(&T), (void*)const_cast<float*>(&scale_log2)};
+template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, bool SPLIT,
+          int QB = 1>
+hipError_t launch_one(AttnArgs a, hipStream_t stream) {
+    constexpr int BR = 32 * QB * NW;
+    a.T = (a.N + BR - 1) / BR;
+    a.scale_log2 = kLog2e / __builtin_sqrtf((float)D);
+    void* params[] = {(void*)&a};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, NW, MINWG, STAGES, DIST, SPLIT>),
-        dim3((unsigned)(T * BH)), dim3(G::THREADS), args, 0, stream);
+        reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, NW, MINWG, STAGES, DIST, SPLIT, QB>),
+        dim3((unsigned)(a.T * a.BH)), dim3(64 * NW), params, 0, stream);
 }
 
 // 8 waves, one workgroup per CU, phase-split, copies two tiles ahead (four
 // stages); or 4 waves, two independent workgroups per CU (LDS for two: copies
 // one tile ahead at D = 128, two at D = 64).
 template <bool BF16, int D, bool CAUSAL>
-hipError_t launch_cfg(const void* q, const void* k, const void* v, float* o, float* lse, int BH,
-                      int N, int waves, hipStream_t stream) {
+hipError_t launch_cfg(const AttnArgs& a, int waves, hipStream_t stream) {
     if (waves == 4) {
         if constexpr (D == 128)
-            return launch_one<BF16, D, CAUSAL, 4, 2, 2, 1, false>(q, k, v, o, lse, BH, N, stream);
+            return launch_one<BF16, D, CAUSAL, 4, 2, 2, 1, false>(a, stream);
         else
-            return launch_one<BF16, D, CAUSAL, 4, 2, 3, 2, false>(q, k, v, o, lse, BH, N, stream);
+            return launch_one<BF16, D, CAUSAL, 4, 2, 3, 2, false>(a, stream);
     }
-    return launch_one<BF16, D, CAUSAL, 8, 1, 4, 2, true>(q, k, v, o, lse, BH, N, stream);
+    return launch_one<BF16, D, CAUSAL, 8, 1, 4, 2, true>(a, stream);
 }
 
 }  // namespace
@@ -569,19 +624,30 @@ int attn_pick_waves(int64_t BH, int64_t N) {
 }
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
-                           int BH, int N, int D, bool causal, bool bf16, int waves, hipStream_t stream) {
+                           int B, int H, int Hkv, int N, int D, bool causal, bool bf16, int waves,
+                           hipStream_t stream) {
+    AttnArgs a{};
+    a.q = static_cast<const u16*>(q);
+    a.k = static_cast<const u16*>(k);
+    a.v = static_cast<const u16*>(v);
+    a.o = o;
+    a.lse = lse;
+    a.BH = B * H;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.N = N;
     if (D == 128) {
         if (bf16)
-            return causal ? launch_cfg<true, 128, true>(q, k, v, o, lse, BH, N, waves, stream)
-                          : launch_cfg<true, 128, false>(q, k, v, o, lse, BH, N, waves, stream);
-        return causal ? launch_cfg<false, 128, true>(q, k, v, o, lse, BH, N, waves, stream)
-                      : launch_cfg<false, 128, false>(q, k, v, o, lse, BH, N, waves, stream);
+            return causal ? launch_cfg<true, 128, true>(a, waves, stream)
+                          : launch_cfg<true, 128, false>(a, waves, stream);
+        return causal ? launch_cfg<false, 128, true>(a, waves, stream)
+                      : launch_cfg<false, 128, false>(a, waves, stream);
     }
     if (bf16)
-        return causal ? launch_cfg<true, 64, true>(q, k, v, o, lse, BH, N, waves, stream)
-                      : launch_cfg<true, 64, false>(q, k, v, o, lse, BH, N, waves, stream);
-    return causal ? launch_cfg<false, 64, true>(q, k, v, o, lse, BH, N, waves, stream)
-                  : launch_cfg<false, 64, false>(q, k, v, o, lse, BH, N, waves, stream);
+        return causal ? launch_cfg<true, 64, true>(a, waves, stream)
+                      : launch_cfg<true, 64, false>(a, waves, stream);
+    return causal ? launch_cfg<false, 64, true>(a, waves, stream)
+                  : launch_cfg<false, 64, false>(a, waves, stream);
 }
 
 }  // namespace osc

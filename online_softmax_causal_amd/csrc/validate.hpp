@@ -24,11 +24,13 @@ inline bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes
     return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
 }
 
+// q, o, lse cover B*H heads; k, v cover B*Hkv heads (Hkv divides H).
 inline attn_status_t validate_attn(const void* q, const void* k, const void* v, const float* o,
-                                   const float* lse, int64_t B, int64_t H, int64_t N, int64_t D,
-                                   attn_dtype_t dtype) {
+                                   const float* lse, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                                   int64_t D, attn_dtype_t dtype) {
     if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
-    if (B < 1 || H < 1 || N < 1 || D < 1) return ATTN_ERR_SHAPE;
+    if (B < 1 || H < 1 || Hkv < 1 || N < 1 || D < 1) return ATTN_ERR_SHAPE;
+    if (Hkv > H || H % Hkv != 0) return ATTN_ERR_SHAPE;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
     int64_t bh = 0, bhn = 0, total = 0, nd = 0;
@@ -41,10 +43,12 @@ inline attn_status_t validate_attn(const void* q, const void* k, const void* v, 
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         !aligned(lse, 4))
         return ATTN_ERR_ALIGN;
-    const int64_t in_bytes = total * 2, o_bytes = total * 4, lse_bytes = bhn * 4;
+    const int64_t q_bytes = total * 2, kv_bytes = (total / H) * Hkv * 2;
+    const int64_t o_bytes = total * 4, lse_bytes = bhn * 4;
     const void* ins[3] = {q, k, v};
-    for (const void* in : ins)
-        if (overlap(o, o_bytes, in, in_bytes) || overlap(lse, lse_bytes, in, in_bytes))
+    const int64_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(o, o_bytes, ins[i], in_bytes[i]) || overlap(lse, lse_bytes, ins[i], in_bytes[i]))
             return ATTN_ERR_ALIAS;
     if (overlap(o, o_bytes, lse, lse_bytes)) return ATTN_ERR_ALIAS;
     return ATTN_OK;

@@ -153,6 +153,41 @@ def attn_rows(q, k, v, causal: bool, rows, nthreads: int | None = None):
     return o, lse
 
 
+def kv_head(h: int, H: int, Hkv: int) -> int:
+    """K/V head read by query head h when H query heads share Hkv K/V heads.
+
+    "CUDA KV Cache: paged storage and long-context decode" (chengzipai.xyz),
+    section 3: with g = H / Hkv query heads per group, query head h reads K/V
+    head floor(h / g).
+    """
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    return h // (H // Hkv)
+
+
+def _kv_for_query_heads(x, H: int) -> np.ndarray:
+    """[B, Hkv, N, D] -> [B, H, N, D]: slot h holds K/V head kv_head(h)."""
+    x = to_f64(x)
+    Hkv = x.shape[1]
+    return np.ascontiguousarray(x[:, [kv_head(h, H, Hkv) for h in range(H)]])
+
+
+def attn_fwd_gqa(q, k, v, causal: bool, nthreads: int | None = None):
+    """Grouped-query attention: q [B,H,N,D], k and v [B,Hkv,N,D].
+
+    Each query head is plain attention (attn_fwd) against its group's K/V head.
+    """
+    H = q.shape[1]
+    return attn_fwd(q, _kv_for_query_heads(k, H), _kv_for_query_heads(v, H), causal, nthreads)
+
+
+def attn_rows_gqa(q, k, v, causal: bool, rows, nthreads: int | None = None):
+    """attn_rows for grouped K/V heads; rows are flat ids (b*H+h)*N+i of the query."""
+    H = q.shape[1]
+    return attn_rows(q, _kv_for_query_heads(k, H), _kv_for_query_heads(v, H), causal, rows,
+                     nthreads)
+
+
 def attn_scores(q, k, causal: bool, i: int) -> np.ndarray:
     """Stage 1 alone: the scaled scores of query row i of one head ([N,D] inputs)."""
     q, k = to_f64(q), to_f64(k)

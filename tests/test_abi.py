@@ -78,6 +78,26 @@ def test_attn_rejects_overlap(kw):
     assert call_attn(**kw) == 6
 
 
+def call_gqa(q=BASE, k=BASE + 64 * MB, v=BASE + 128 * MB, o=BASE + 192 * MB,
+             lse=BASE + 320 * MB, B=1, H=8, Hkv=2, N=64, D=128, causal=1, dtype=0):
+    return osc.load().attn_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [dict(Hkv=0), dict(Hkv=-2), dict(Hkv=3), dict(Hkv=16),
+                                dict(H=6, Hkv=4), dict(H=0, Hkv=1)])
+def test_gqa_rejects_bad_head_counts(kw):
+    assert call_gqa(**kw) == 2
+
+
+def test_gqa_other_rejections():
+    assert call_gqa(k=None) == 1
+    assert call_gqa(D=96) == 3
+    assert call_gqa(v=BASE + 128 * MB + 8) == 4
+    # K holds B*Hkv = 2 heads of 64x128 fp16 = 32 KiB: an output 16 KiB into K overlaps it.
+    assert call_gqa(o=BASE + 64 * MB + 16 * 1024) == 6
+    assert call_gqa(lse=BASE + 128 * MB + 32 * 1024 - 4) == 6
+
+
 def call_softmax(x=BASE, y=BASE + 64 * MB, M=4, N=100):
     return osc.load().row_softmax(x, y, M, N, None)
 

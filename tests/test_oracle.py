@@ -264,6 +264,53 @@ def test_matches_torch_sdpa_float64(N, D, causal):
     np.testing.assert_allclose(lse, torch.logsumexp(logits, dim=-1).numpy(), rtol=0, atol=1e-12)
 
 
+# ------------------------------------------------------ grouped K/V heads
+
+def gqa_sdpa_check(q, k, v, causal):
+    """Oracle GQA against torch's float64 SDPA with its own grouped-head mapping."""
+    o, lse = oracle.attn_fwd_gqa(q, k, v, causal)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                           enable_gqa=True)
+    return np.abs(o - ref.numpy()).max()
+
+
+@pytest.mark.parametrize("H,Hkv", [(6, 1), (6, 2), (6, 3), (8, 4)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_gqa_matches_torch_sdpa_enable_gqa(H, Hkv, causal):
+    """Independent library routine: torch SDPA with enable_gqa (query head h uses
+    K/V head h // (H / Hkv)), float64 on the CPU."""
+    B, N, D = 2, 19, 16
+    q = rand(B, H, N, D, scale=2.0)
+    k, v = rand(B, Hkv, N, D, scale=2.0), rand(B, Hkv, N, D)
+    assert gqa_sdpa_check(q, k, v, causal) <= 1e-12
+
+
+def test_gqa_with_one_group_per_head_is_attn_fwd():
+    """Hkv = H reduces to plain attention, bit for bit."""
+    q, k, v = rand(1, 4, 11, 8), rand(1, 4, 11, 8), rand(1, 4, 11, 8)
+    o1, l1 = oracle.attn_fwd_gqa(q, k, v, True)
+    o2, l2 = oracle.attn_fwd(q, k, v, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_gqa_head_map_and_rows_entry():
+    """The head map of the KV-cache page (h_kv = floor(h / g)) on a worked case,
+    and the row-subset entry point agreeing with the full one."""
+    assert [oracle.kv_head(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [oracle.kv_head(h, 6, 3) for h in range(6)] == [0, 0, 1, 1, 2, 2]
+    assert [oracle.kv_head(h, 5, 1) for h in range(5)] == [0] * 5
+    with pytest.raises(ValueError):
+        oracle.kv_head(0, 6, 4)
+    B, H, Hkv, N, D = 2, 4, 2, 9, 8
+    q, k, v = rand(B, H, N, D), rand(B, Hkv, N, D), rand(B, Hkv, N, D)
+    o, lse = oracle.attn_fwd_gqa(q, k, v, False)
+    rows = [0, 8, 9, 40, 71]
+    orow, lrow = oracle.attn_rows_gqa(q, k, v, False, rows)
+    assert np.array_equal(orow, o.reshape(-1, D)[rows])
+    assert np.array_equal(lrow, lse.reshape(-1)[rows])
+
+
 def test_rows_entry_and_thread_count_are_bitwise_stable():
     """The row-subset entry point and any thread count give bit-identical results."""
     B, H, N, D = 1, 3, 40, 16

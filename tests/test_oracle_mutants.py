@@ -97,3 +97,14 @@ def test_unmodified_copy_passes_every_pin(tmp_path):
     finally:
         oracle.swap_library(None)
     assert failed == []
+
+
+def test_gqa_pin_catches_wrong_head_map(monkeypatch):
+    """Planted in the oracle's Python head map: h % Hkv (interleaved groups) in
+    place of h // g.  The torch enable_gqa pin must reject it."""
+    from tests.test_oracle import gqa_sdpa_check, rand
+    q = rand(1, 4, 9, 8, scale=2.0)
+    k, v = rand(1, 2, 9, 8, scale=2.0), rand(1, 2, 9, 8)
+    assert gqa_sdpa_check(q, k, v, True) <= 1e-12
+    monkeypatch.setattr(oracle, "kv_head", lambda h, H, Hkv: h % Hkv)
+    assert gqa_sdpa_check(q, k, v, True) > 1e-3

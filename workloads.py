@@ -37,6 +37,11 @@ class AttnWorkload:
     sigma_qk: float
     sigma_v: float
     seed: int
+    Hkv: int | None = None   # K/V heads (grouped-query attention); None = H
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
 
     @property
     def flops(self) -> float:
@@ -44,8 +49,9 @@ class AttnWorkload:
         return attn_flops(self.B, self.H, self.N, self.D, self.causal)
 
     def describe(self) -> str:
-        return "%s attn fwd %s B%d H%d N%d D%d" % (
-            "causal" if self.causal else "non-causal", self.dtype, self.B, self.H, self.N, self.D)
+        heads = "H%d" % self.H if self.Hkv is None else "Hq%d Hkv%d" % (self.H, self.Hkv)
+        return "%s attn fwd %s B%d %s N%d D%d" % (
+            "causal" if self.causal else "non-causal", self.dtype, self.B, heads, self.N, self.D)
 
 
 @dataclass(frozen=True)
@@ -77,6 +83,14 @@ ATTN = {
     "C5": AttnWorkload("C5", 4, 32, 4095, 64, False, "bf16", 1.0, 1.0, 47),
 }
 
+# Grouped-query attention: 32 query heads sharing 8 K/V heads at D=128 (the
+# head configuration of the KV-cache page's decode measurements, section 3),
+# at the FA page's longest prefill length.
+GQA = {
+    "G1": AttnWorkload("G1", 1, 32, 8192, 128, True, "f16", 1.0, 1.0, 50, Hkv=8),
+    "G2": AttnWorkload("G2", 2, 8, 1000, 64, False, "bf16", 2.0, 1.0, 51, Hkv=1),
+}
+
 SOFTMAX = {
     "R1": SoftmaxWorkload("R1", 1025, 257, 80.0, 48),
     "R2": SoftmaxWorkload("R2", 8192, 32768, 80.0, 49),
@@ -98,7 +112,21 @@ def attn_inputs(B: int, H: int, N: int, D: int, dtype: str, seed: int,
     return q.contiguous(), k.contiguous(), v.contiguous()
 
 
+def gqa_inputs(B: int, H: int, Hkv: int, N: int, D: int, dtype: str, seed: int,
+               sigma_qk: float = 1.0, sigma_v: float = 1.0):
+    """Q [B,H,N,D] and K, V [B,Hkv,N,D] (same recipe and draw order as attn_inputs)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    td = TORCH_DTYPE[dtype]
+    q = (torch.randn((B, H, N, D), generator=g, dtype=torch.float32) * sigma_qk).to(td)
+    k = (torch.randn((B, Hkv, N, D), generator=g, dtype=torch.float32) * sigma_qk).to(td)
+    v = (torch.randn((B, Hkv, N, D), generator=g, dtype=torch.float32) * sigma_v).to(td)
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
 def workload_inputs(w: AttnWorkload):
+    if w.Hkv is not None:
+        return gqa_inputs(w.B, w.H, w.Hkv, w.N, w.D, w.dtype, w.seed, w.sigma_qk, w.sigma_v)
     return attn_inputs(w.B, w.H, w.N, w.D, w.dtype, w.seed, w.sigma_qk, w.sigma_v)
 
 
