@@ -17,8 +17,9 @@ One JSON line goes to stdout.  Besides the contract fields it carries:
   cpu_baseline  the FP64 oracle timed on this host's cores on a bounded
                 sample of the same workload (every s-th query row);
   parity_sample max-abs error of the GPU output on those sampled rows;
-  extra         the other configurations (C1, C2, C3, C5 attention; R1, R2
-                row softmax), timed as the median of 7 group means of
+  extra         the other configurations (C1, C2, C3, C5 attention; G1
+                grouped-query attention; S1 without and with the key split;
+                R1, R2 row softmax), timed as the median of 7 group means of
                 back-to-back launches (FA page, section 8 method).
 Runs on one GPU only; --gpus above 1 exits with a message.
 """
@@ -103,6 +104,39 @@ def extra_configs(dev):
         out[name] = {"workload": w.describe(), "ms": round(med, 5), "ms_min": round(mn, 5),
                      "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
         del q, k, v, o, lse
+    # Grouped-query attention (K/V heads shared by groups of query heads).
+    w = workloads.GQA["G1"]
+    q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
+    o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    fn = lambda: osc.attn_fwd_gqa(q, k, v, o, lse, w.B, w.H, w.Hkv, w.N, w.D, w.causal, w.dtype)
+    med, mn = time_groups(fn, stream)
+    tf = w.flops / (med * 1e-3) / 1e12
+    out["G1"] = {"workload": w.describe(), "entry": "attn_fwd_gqa", "ms": round(med, 5),
+                 "ms_min": round(mn, 5), "tflops": round(tf, 2),
+                 "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+    del q, k, v, o, lse
+    # Long sequence, few heads: plain launch against the automatic key split
+    # (both kernels, attention and merge, inside the timed region).
+    w = workloads.SPLITKV["S1"]
+    q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
+    o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    need = osc.attn_fwd_splitkv_workspace(w.B, w.H, w.N, w.D, w.causal, 0)
+    ws = torch.empty((max(need, 16) // 4,), dtype=torch.float32, device=dev)
+    for entry, fn in (
+            ("attn_fwd", lambda: osc.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.D, w.causal,
+                                              w.dtype)),
+            ("attn_fwd_splitkv", lambda: osc.attn_fwd_splitkv(q, k, v, o, lse, w.B, w.H, w.H, w.N,
+                                                              w.D, w.causal, w.dtype, 0, ws,
+                                                              need))):
+        med, mn = time_groups(fn, stream)
+        tf = w.flops / (med * 1e-3) / 1e12
+        out["S1 " + entry] = {"workload": w.describe(), "entry": entry, "ms": round(med, 5),
+                              "ms_min": round(mn, 5), "tflops": round(tf, 2),
+                              "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4),
+                              "workspace_bytes": need if entry != "attn_fwd" else 0}
+    del q, k, v, o, lse, ws
     for name in ("R1", "R2"):
         w = workloads.SOFTMAX[name]
         x = workloads.softmax_inputs(w.M, w.N, seed=w.seed, last=w.last).to(dev)

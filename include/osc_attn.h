@@ -60,8 +60,12 @@ typedef enum {
     ATTN_ERR_UNSUPPORTED = 3, /* head dim not 64 or 128, or unknown dtype */
     ATTN_ERR_ALIGN = 4,       /* a pointer is not aligned as required below */
     ATTN_ERR_LAUNCH = 5,      /* the HIP runtime refused the kernel launch */
-    ATTN_ERR_ALIAS = 6        /* an output buffer overlaps an input buffer */
+    ATTN_ERR_ALIAS = 6,       /* an output or workspace buffer overlaps another buffer */
+    ATTN_ERR_WORKSPACE = 7    /* the workspace is smaller than the call needs */
 } attn_status_t;
+
+/* Largest segment count attn_fwd_splitkv accepts. */
+#define ATTN_MAX_SPLITS 64
 
 /*
  * attn_fwd - attention forward for B*H independent heads.
@@ -110,6 +114,45 @@ attn_status_t attn_fwd(const void *q, const void *k, const void *v, float *o, fl
 attn_status_t attn_fwd_gqa(const void *q, const void *k, const void *v, float *o, float *lse,
                            int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal,
                            attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * attn_fwd_splitkv - attention forward with the keys of every head split into
+ * segments (split-KV).
+ *
+ * Each workgroup handles one query tile against one key segment and stores
+ * that segment's partial state (m, l, unnormalised o) in the workspace; a
+ * second kernel then merges the segments of each row with
+ * m = max_s m_s, l = sum_s l_s e^(m_s - m), O = sum_s o_s e^(m_s - m) / l
+ * ("CUDA KV Cache: paged storage and long-context decode" (chengzipai.xyz),
+ * section 7; FA page, section 7: split along K for long sequences with few
+ * heads).  The result is the attn_fwd_gqa result up to rounding.  Both
+ * kernels are enqueued on `stream`.
+ *
+ *   q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype  as for attn_fwd_gqa.
+ *   num_splits  0: the library chooses (one segment when B*H and N already
+ *               fill the GPU, else up to 16); 1..ATTN_MAX_SPLITS: that many
+ *               segments at most.  Segments hold a multiple of 256 keys, so
+ *               fewer may be used for short N.  Larger values: ATTN_ERR_SHAPE.
+ *   workspace   device buffer owned by the caller, 16-byte aligned, of at
+ *               least attn_fwd_splitkv_workspace(B, H, N, D, causal,
+ *               num_splits) bytes; it must not overlap q, k, v, o or lse.
+ *               Its contents on entry do not matter and are undefined after
+ *               the call.  May be NULL when that size is 0 (one segment).
+ *               Two calls that run at the same time need separate workspaces.
+ *   workspace_bytes  size of `workspace`; too small: ATTN_ERR_WORKSPACE.
+ */
+attn_status_t attn_fwd_splitkv(const void *q, const void *k, const void *v, float *o, float *lse,
+                               int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal,
+                               attn_dtype_t dtype, int num_splits, void *workspace,
+                               int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_fwd_splitkv_workspace - bytes of workspace attn_fwd_splitkv needs for
+ * these sizes (0 if it uses one segment), or -1 if the sizes or num_splits
+ * are invalid.  Pure host computation; enqueues nothing.
+ */
+int64_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                                   int num_splits);
 
 /*
  * row_softmax - y[r, :] = softmax(x[r, :]) for r < M.

@@ -10,6 +10,9 @@ The entry points mirror the C ABI in ``include/osc_attn.h``:
     attn_fwd(q, k, v, o, lse, B, H, N, D, causal, dtype, stream=None)
     row_softmax(x, y, M, N, stream=None)
     attn_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, stream=None)
+    attn_fwd_splitkv(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, num_splits,
+                     workspace, workspace_bytes, stream=None)
+    attn_fwd_splitkv_workspace(B, H, N, D, causal, num_splits=0)
     attn_status_str(status)
 
 Pointer arguments accept device tensors (``torch.Tensor``, only its address is
@@ -36,8 +39,10 @@ STATUS = {
     4: "ATTN_ERR_ALIGN",
     5: "ATTN_ERR_LAUNCH",
     6: "ATTN_ERR_ALIAS",
+    7: "ATTN_ERR_WORKSPACE",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_gqa", "row_softmax", "attn_status_str")
+EXPORTS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace",
+           "row_softmax", "attn_status_str")
 
 _lib = None
 
@@ -64,6 +69,11 @@ def load():
     lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
                                  ctypes.c_int, vp]
     lib.attn_fwd_gqa.restype = ctypes.c_int
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    lib.attn_fwd_splitkv.restype = ctypes.c_int
+    lib.attn_fwd_splitkv_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.attn_fwd_splitkv_workspace.restype = i64
     lib.row_softmax.argtypes = [vp, vp, i64, i64, vp]
     lib.row_softmax.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
@@ -122,6 +132,23 @@ def attn_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, stream=None) -
                              _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_fwd_gqa")
+
+
+def attn_fwd_splitkv_workspace(B, H, N, D, causal, num_splits=0) -> int:
+    """Workspace bytes attn_fwd_splitkv needs (0: one segment, no workspace); -1 if invalid."""
+    return int(load().attn_fwd_splitkv_workspace(int(B), int(H), int(N), int(D),
+                                                 int(bool(causal)), int(num_splits)))
+
+
+def attn_fwd_splitkv(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, num_splits, workspace,
+                     workspace_bytes, stream=None) -> None:
+    """Enqueue split-KV attention forward (partial states in `workspace`, then a merge)."""
+    st = load().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                 int(Hkv), int(N), int(D), int(bool(causal)), _dtype(dtype),
+                                 int(num_splits), _ptr(workspace), int(workspace_bytes),
+                                 _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_splitkv")
 
 
 def row_softmax(x, y, M, N, stream=None) -> None:

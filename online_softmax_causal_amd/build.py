@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libosc_attn.so")
-SOURCES = ["attn_fwd.hip", "row_softmax.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "splitkv.hip", "row_softmax.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -15,7 +15,54 @@ static attn_status_t attn_fwd_impl(const void* q, const void* k, const void* v, 
     if (st != ATTN_OK) return st;
     const int waves = osc::attn_pick_waves(B * H, N);
     const hipError_t e = osc::launch_attn_fwd(q, k, v, o, lse, (int)B, (int)H, (int)Hkv, (int)N,
-                                              (int)D, causal != 0, dtype == ATTN_BF16, waves, stream);
+                                              (int)D, causal != 0, dtype == ATTN_BF16, waves,
+                                              nullptr, nullptr, nullptr, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+// Split plan and workspace size for valid sizes; false if they are not.
+static bool splitkv_plan(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int num_splits,
+                         osc::SplitPlan* plan, int64_t* bytes) {
+    if (B < 1 || H < 1 || N < 1 || (D != 64 && D != 128)) return false;
+    if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return false;
+    int64_t bh = 0, bhn = 0, total = 0;
+    if (!osc::mul_below_2_62(B, H, &bh) || !osc::mul_below_2_62(bh, N, &bhn) ||
+        !osc::mul_below_2_62(bhn, D + 2, &total) || N * D >= (int64_t(1) << 31) ||
+        bh >= (int64_t(1) << 31))
+        return false;
+    *plan = osc::attn_plan_split(bh, N, causal != 0, num_splits);
+    int64_t words = 0;
+    if (!osc::mul_below_2_62(total, plan->nseg, &words) || words >= (int64_t(1) << 60)) return false;
+    // One workgroup per (query tile of at least 128 rows, head, segment).
+    if (bh * ((N + 127) / 128) * plan->nseg >= (int64_t(1) << 31)) return false;
+    *bytes = osc::splitkv_workspace_bytes(*plan, bh, N, D);
+    return true;
+}
+
+int64_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t D, int causal,
+                                   int num_splits) {
+    osc::SplitPlan plan;
+    int64_t bytes = 0;
+    return splitkv_plan(B, H, N, D, causal, num_splits, &plan, &bytes) ? bytes : -1;
+}
+
+attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, float* o, float* lse,
+                               int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal,
+                               attn_dtype_t dtype, int num_splits, void* workspace,
+                               int64_t workspace_bytes, hipStream_t stream) {
+    attn_status_t st = osc::validate_attn(q, k, v, o, lse, B, H, Hkv, N, D, dtype);
+    if (st != ATTN_OK) return st;
+    osc::SplitPlan plan;
+    int64_t need = 0;
+    if (!splitkv_plan(B, H, N, D, causal, num_splits, &plan, &need)) return ATTN_ERR_SHAPE;
+    st = osc::validate_workspace(workspace, workspace_bytes, need, q, k, v, o, lse, B, H, Hkv, N, D);
+    if (st != ATTN_OK) return st;
+    float* part_o = static_cast<float*>(workspace);
+    float2* part_ml = plan.nseg > 1 ? reinterpret_cast<float2*>(part_o + plan.nseg * B * H * N * D)
+                                    : nullptr;
+    const hipError_t e = osc::launch_attn_fwd(q, k, v, o, lse, (int)B, (int)H, (int)Hkv, (int)N,
+                                              (int)D, causal != 0, dtype == ATTN_BF16, plan.waves,
+                                              &plan, part_o, part_ml, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -47,6 +94,7 @@ const char* attn_status_str(attn_status_t status) {
         case ATTN_ERR_ALIGN: return "a pointer is not aligned as required";
         case ATTN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
         case ATTN_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+        case ATTN_ERR_WORKSPACE: return "the workspace is smaller than the call needs";
     }
     return "unknown status";
 }

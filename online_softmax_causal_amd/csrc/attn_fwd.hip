@@ -153,6 +153,14 @@ struct AttnArgs {
     int N;          // sequence length
     int T;          // query tiles per head
     float scale_log2;  // log2(e) / sqrt(D)
+    // Split along the keys (split-KV): segment s of every head covers the
+    // 64-key tiles [s * seg_tiles, (s + 1) * seg_tiles).  With part_o set,
+    // each workgroup stores its segment's unnormalised state instead of O
+    // and LSE, for splitkv_merge_kernel to combine.
+    int nseg;          // segments per head (1: no split)
+    int seg_tiles;     // tiles per segment, a multiple of 4 (256 keys)
+    float* part_o;     // [nseg, B*H, N, D]: sum_j 2^(s_j - m) v_j over the segment
+    float2* part_ml;   // [nseg, B*H, N]: (m, l) of the segment, base-2 units
 };
 
 template <int D, int QB>
@@ -434,8 +442,12 @@ attn_fwd_kernel(AttnArgs args) {
     // BH is a multiple of 8, XCD x takes the contiguous heads
     // [x BH/8, (x+1) BH/8) of every query tile, so all query tiles of a head,
     // and the query heads that share a K/V head, meet in one L2.
+    // With a key split the segments of one query tile follow each other.
     const int bid = blockIdx.x;
-    const int t = CAUSAL ? (args.T - 1 - bid / args.BH) : (bid / args.BH);
+    const int per_tile = args.BH * args.nseg;
+    const int tt = bid / per_tile;
+    const int t = CAUSAL ? (args.T - 1 - tt) : tt;
+    const int seg = (bid - tt * per_tile) / args.BH;
     const int j = bid % args.BH;
     const int bh = (args.BH & 7) ? j : (j & 7) * (args.BH >> 3) + (j >> 3);
     // Query head h of batch b reads K/V head h / (H / Hkv) of the same batch
@@ -453,10 +465,17 @@ attn_fwd_kernel(AttnArgs args) {
     int row0[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) row0[b] = row_base + (QB * block + b) * 32;
-    const int kv_end = CAUSAL ? min(row_base + BR, N) : N;
+    // Key tiles of this workgroup: kt0 .. ntiles-1.  Segments hold a whole
+    // number of query tiles' worth of keys (seg_tiles * 64 is a multiple of
+    // BR), so a segment either starts at or before the first row of the query
+    // tile, and every row sees at least one of its keys, or lies entirely in
+    // the masked future of the tile and the workgroup has nothing to do.
+    const int kt0 = seg * args.seg_tiles;
+    const int kv_end = min(CAUSAL ? min(row_base + BR, N) : N, (kt0 + args.seg_tiles) * G::BC);
     const int ntiles = (kv_end + G::BC - 1) / G::BC;
-    // Tiles this wave attends to: 0 .. last_live (none if its rows are past N).
-    const int last_live = row0[0] >= N ? -1
+    if (kt0 >= ntiles) return;
+    // Tiles this wave attends to: kt0 .. last_live (none if its rows are past N).
+    const int last_live = row0[0] >= N ? kt0 - 1
                         : min(ntiles - 1, CAUSAL ? (row0[QB - 1] + 31) / G::BC : ntiles - 1);
 
     WaveState<D, QB> st;
@@ -517,14 +536,14 @@ attn_fwd_kernel(AttnArgs args) {
     // Prologue: the first DIST tiles are copied while the Q fragments arrive;
     // one full wait covers both (and tells the compiler Q is ready).
 #pragma unroll
-    for (int i = 0; i < DIST; ++i) issue(i);
+    for (int i = 0; i < DIST; ++i) issue(kt0 + i);
     wait_vmcnt<0>();
     __syncthreads();
 
     // All waves run all ntiles iterations (copies and barriers), whatever
     // they compute; the loops are split so each holds one code variant.
     f32x16 s[QB][2];
-    int it = 0;
+    int it = kt0;
     if (!lagging) {
         for (; it < last_live; ++it) {
             issue(it + DIST);
@@ -540,11 +559,11 @@ attn_fwd_kernel(AttnArgs args) {
             ++it;
         }
     } else {
-        if (last_live >= 0) {
-            issue(DIST);
-            qk(0, s);
-            finish(0);
-            it = 1;
+        if (last_live >= kt0) {
+            issue(kt0 + DIST);
+            qk(kt0, s);
+            finish(kt0);
+            it = kt0 + 1;
             for (; it <= last_live; ++it) {
                 issue(it + DIST);
                 smpv(it - 1, s);
@@ -566,7 +585,31 @@ attn_fwd_kernel(AttnArgs args) {
         finish(it);
     }
 
-    // Epilogue: combine the two lane halves of each query, normalise, store.
+    // Epilogue: combine the two lane halves of each query, normalise, store;
+    // or, for one segment of a key split, store the unnormalised state.
+    if (args.part_o != nullptr) {
+        const int64_t part = (int64_t)seg * args.BH + bh;
+        float* po = args.part_o + part * N * D;
+        float2* pml = args.part_ml + part * N;
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            const float l_tot = st.l[b] + swap32_f32(st.l[b]);
+            const int row = row0[b] + col;
+            if (row < N) {
+                float* orow = po + (int64_t)row * D;
+#pragma unroll
+                for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        const f32x4 r = {st.acc[b][mt][4 * i4 + 0], st.acc[b][mt][4 * i4 + 1],
+                                         st.acc[b][mt][4 * i4 + 2], st.acc[b][mt][4 * i4 + 3]};
+                        *reinterpret_cast<f32x4*>(orow + mt * 32 + 8 * i4 + 4 * g) = r;
+                    }
+                if (g == 0) pml[row] = float2{st.m[b], l_tot};
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
         const float l_tot = st.l[b] + swap32_f32(st.l[b]);
@@ -596,7 +639,7 @@ hipError_t launch_one(AttnArgs a, hipStream_t stream) {
     void* params[] = {(void*)&a};
     return hipLaunchKernel(
         reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, NW, MINWG, STAGES, DIST, SPLIT, QB>),
-        dim3((unsigned)(a.T * a.BH)), dim3(64 * NW), params, 0, stream);
+        dim3((unsigned)(a.T * a.BH * a.nseg)), dim3(64 * NW), params, 0, stream);
 }
 
 // 8 waves, one workgroup per CU, phase-split, copies two tiles ahead (four
@@ -625,6 +668,7 @@ int attn_pick_waves(int64_t BH, int64_t N) {
 
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
                            int B, int H, int Hkv, int N, int D, bool causal, bool bf16, int waves,
+                           const SplitPlan* split, float* part_o, float2* part_ml,
                            hipStream_t stream) {
     AttnArgs a{};
     a.q = static_cast<const u16*>(q);
@@ -636,18 +680,73 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o
     a.H = H;
     a.Hkv = Hkv;
     a.N = N;
+    if (split != nullptr && split->nseg > 1) {
+        a.nseg = split->nseg;
+        a.seg_tiles = split->seg_tiles;
+        a.part_o = part_o;
+        a.part_ml = part_ml;
+    } else {
+        a.nseg = 1;
+        a.seg_tiles = ((N + 255) / 256) * 4;
+    }
+    hipError_t e;
     if (D == 128) {
         if (bf16)
-            return causal ? launch_cfg<true, 128, true>(a, waves, stream)
-                          : launch_cfg<true, 128, false>(a, waves, stream);
-        return causal ? launch_cfg<false, 128, true>(a, waves, stream)
-                      : launch_cfg<false, 128, false>(a, waves, stream);
+            e = causal ? launch_cfg<true, 128, true>(a, waves, stream)
+                       : launch_cfg<true, 128, false>(a, waves, stream);
+        else
+            e = causal ? launch_cfg<false, 128, true>(a, waves, stream)
+                       : launch_cfg<false, 128, false>(a, waves, stream);
+    } else {
+        if (bf16)
+            e = causal ? launch_cfg<true, 64, true>(a, waves, stream)
+                       : launch_cfg<true, 64, false>(a, waves, stream);
+        else
+            e = causal ? launch_cfg<false, 64, true>(a, waves, stream)
+                       : launch_cfg<false, 64, false>(a, waves, stream);
     }
-    if (bf16)
-        return causal ? launch_cfg<true, 64, true>(a, waves, stream)
-                      : launch_cfg<true, 64, false>(a, waves, stream);
-    return causal ? launch_cfg<false, 64, true>(a, waves, stream)
-                  : launch_cfg<false, 64, false>(a, waves, stream);
+    if (e != hipSuccess || a.nseg == 1) return e;
+    return launch_splitkv_merge(part_o, part_ml, o, lse, a.BH, N, D, a.nseg, a.seg_tiles * 64, causal,
+                                stream);
+}
+
+// Split-KV plan (KV page, section 7: split the keys when the query side
+// alone cannot fill the chip; the count depends on B*H, length and the
+// number of CUs).  `requested` > 0 asks for that many segments.  With 0 the
+// plan keeps one segment when the plain grid has two workgroups per CU or N
+// is below 4096 keys (the merge's extra launch and traffic cost more than a
+// short head gains).  Otherwise it takes the most segments whose non-empty
+// workgroups still fit on the CUs at once (one 8-wave workgroup per CU):
+// more would add a second round of workgroups, each paying its own Q load
+// and partial-state store, plus merge traffic.  With causal masking, S
+// segments leave about (S + 1) / 2 of the grid non-empty.  At most 16.
+// Segments are whole multiples of 256 keys (so they align with every
+// query-tile size); the count is then the number of such segments N needs.
+// A split runs 8-wave workgroups: the segments supply the parallelism, and
+// 256 query rows share each K/V tile.
+SplitPlan attn_plan_split(int64_t BH, int64_t N, bool causal, int requested) {
+    constexpr int kCUs = 256;
+    const int64_t tiles = (N + 63) / 64;
+    const int64_t quads = (tiles + 3) / 4;     // 256-key units
+    const int plain_waves = attn_pick_waves(BH, N);
+    const int64_t wgs_plain = BH * ((N + 32 * plain_waves - 1) / (32 * plain_waves));
+    const int64_t wgs8 = BH * ((N + 255) / 256);
+    int64_t want = requested;
+    if (want <= 0) {
+        if (wgs_plain >= 2 * kCUs || N < 4096)
+            want = 1;
+        else
+            want = causal ? 2 * kCUs / wgs8 - 1 : kCUs / wgs8;
+        want = want > 16 ? 16 : want;
+    }
+    if (want > quads) want = quads;
+    if (want < 1) want = 1;
+    const int64_t seg_quads = (quads + want - 1) / want;
+    SplitPlan p;
+    p.seg_tiles = (int)(seg_quads * 4);
+    p.nseg = (int)((quads + seg_quads - 1) / seg_quads);
+    p.waves = p.nseg > 1 ? 8 : plain_waves;
+    return p;
 }
 
 }  // namespace osc

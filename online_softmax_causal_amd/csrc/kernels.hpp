@@ -11,10 +11,34 @@ namespace osc {
 // Waves per workgroup (4 or 8) for a problem of BH heads of N rows.
 int attn_pick_waves(int64_t BH, int64_t N);
 
+// A split of every head's keys into nseg segments of seg_tiles 64-key tiles.
+struct SplitPlan {
+    int nseg;       // segments (1: no split)
+    int seg_tiles;  // tiles per segment, a multiple of 4
+    int waves;      // waves per workgroup of the attention kernel
+};
+
+// Segments for a key split; requested = 0 chooses automatically.
+SplitPlan attn_plan_split(int64_t BH, int64_t N, bool causal, int requested);
+
+// Bytes of workspace a split needs: the partial output and (m, l) per segment.
+inline int64_t splitkv_workspace_bytes(const SplitPlan& p, int64_t BH, int64_t N, int64_t D) {
+    return p.nseg <= 1 ? 0 : (int64_t)p.nseg * BH * N * (D + 2) * 4;
+}
+
 // q, o, lse: B*H heads; k, v: B*Hkv heads, query head h reads K/V head h / (H / Hkv).
+// With split->nseg > 1, part_o [nseg, B*H, N, D] and part_ml [nseg, B*H, N]
+// receive the segments' states and a second kernel merges them into o, lse.
 hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
                            int B, int H, int Hkv, int N, int D, bool causal, bool bf16, int waves,
+                           const SplitPlan* split, float* part_o, float2* part_ml,
                            hipStream_t stream);
+
+// o, lse of every row from the states of its live segments (key segments of
+// seg_rows keys; with causal masking row i has floor(i / seg_rows) + 1).
+hipError_t launch_splitkv_merge(const float* part_o, const float2* part_ml, float* o, float* lse,
+                                int BH, int N, int D, int nseg, int seg_rows, bool causal,
+                                hipStream_t stream);
 
 hipError_t launch_row_softmax(const float* x, float* y, int64_t M, int64_t N, hipStream_t stream);
 

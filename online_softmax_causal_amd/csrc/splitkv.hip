@@ -1,0 +1,72 @@
+// Second kernel of split-KV attention: merge the per-segment states of each
+// query row into O and LSE (gfx950).
+//
+// Segment s of a row holds (m_s, l_s, o_s): m_s is the reference maximum of
+// its scaled logits in base-2 units, l_s = sum_j 2^(x_j - m_s) and
+// o_s = sum_j 2^(x_j - m_s) v_j over the segment's visible keys.  The row's
+// result follows the split-KV merge of "CUDA KV Cache: paged storage and
+// long-context decode" (chengzipai.xyz), section 7:
+//     m = max_s m_s,  l = sum_s l_s 2^(m_s - m),  O = sum_s o_s 2^(m_s - m) / l,
+// the same law as the tile recurrence (FA page, section 4), folded here one
+// segment at a time with the shared online_rescale.  LSE = (m + log2 l) ln 2.
+//
+// The kernel is bound by HBM: per row it reads nseg * (D + 2) * 4 bytes and
+// writes (D + 1) * 4.  D / 4 lanes cover one row with 16-byte accesses.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+#include "online_merge.hpp"
+
+namespace osc {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+__global__ void __launch_bounds__(256)
+splitkv_merge_kernel(const float* __restrict__ part_o, const float2* __restrict__ part_ml,
+                     float* __restrict__ o, float* __restrict__ lse, int64_t rows, int N, int nseg,
+                     int seg_rows, bool causal) {
+    constexpr int TPR = D / 4;           // lanes per row
+    constexpr int RPB = 256 / TPR;       // rows per workgroup
+    const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c = (threadIdx.x % TPR) * 4;
+    if (r >= rows) return;
+    const int i = (int)(r % N);
+    // Segments with a visible key: all of them, or with causal masking those
+    // starting at or before row i.
+    const int live = causal ? min(nseg, i / seg_rows + 1) : nseg;
+    float m = -INFINITY, l = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < live; ++s) {
+        const int64_t pr = (int64_t)s * rows + r;
+        const float2 ml = part_ml[pr];
+        const f32x4 os = *reinterpret_cast<const f32x4*>(part_o + pr * D + c);
+        const float mn = fmaxf(m, ml.x);
+        const float a = online_rescale(m, mn), b = online_rescale(ml.x, mn);
+        l = l * a + ml.y * b;
+        acc = acc * a + os * b;
+        m = mn;
+    }
+    const float inv = 1.0f / l;
+    *reinterpret_cast<f32x4*>(o + r * D + c) = acc * inv;
+    if (c == 0) lse[r] = (m + log2f(l)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_splitkv_merge(const float* part_o, const float2* part_ml, float* o, float* lse,
+                                int BH, int N, int D, int nseg, int seg_rows, bool causal,
+                                hipStream_t stream) {
+    const int64_t rows = (int64_t)BH * N;
+    const int rpb = 256 / (D / 4);
+    const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+    int64_t rows_a = rows;
+    void* params[] = {(void*)&part_o, (void*)&part_ml, (void*)&o, (void*)&lse, (void*)&rows_a,
+                      (void*)&N, (void*)&nseg, (void*)&seg_rows, (void*)&causal};
+    const void* fn = D == 128 ? reinterpret_cast<const void*>(&splitkv_merge_kernel<128>)
+                              : reinterpret_cast<const void*>(&splitkv_merge_kernel<64>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(256), params, 0, stream);
+}
+
+}  // namespace osc

@@ -54,6 +54,24 @@ inline attn_status_t validate_attn(const void* q, const void* k, const void* v, 
     return ATTN_OK;
 }
 
+// Workspace of a split-KV call that needs `need` bytes (0: none is used).
+// The attention arguments have been validated already.
+inline attn_status_t validate_workspace(const void* ws, int64_t ws_bytes, int64_t need,
+                                        const void* q, const void* k, const void* v,
+                                        const float* o, const float* lse, int64_t B, int64_t H,
+                                        int64_t Hkv, int64_t N, int64_t D) {
+    if (need == 0) return ATTN_OK;
+    if (!ws) return ATTN_ERR_NULL;
+    if (!aligned(ws, 16)) return ATTN_ERR_ALIGN;
+    if (ws_bytes < need) return ATTN_ERR_WORKSPACE;
+    const int64_t total = B * H * N * D;
+    const int64_t kv = B * Hkv * N * D * 2;
+    if (overlap(ws, need, q, total * 2) || overlap(ws, need, k, kv) || overlap(ws, need, v, kv) ||
+        overlap(ws, need, o, total * 4) || overlap(ws, need, lse, B * H * N * 4))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
 inline attn_status_t validate_softmax(const float* x, const float* y, int64_t M, int64_t N) {
     if (!x || !y) return ATTN_ERR_NULL;
     if (M < 1 || N < 1) return ATTN_ERR_SHAPE;

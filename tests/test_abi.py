@@ -98,6 +98,52 @@ def test_gqa_other_rejections():
     assert call_gqa(lse=BASE + 128 * MB + 32 * 1024 - 4) == 6
 
 
+def test_splitkv_workspace_sizes():
+    """Bytes = segments * B*H*N*(D+2)*4; segments are whole 256-key units."""
+    f = osc.attn_fwd_splitkv_workspace
+    row = lambda B, H, N, D: B * H * N * (D + 2) * 4
+    assert f(1, 2, 16384, 128, 1, 0) == 3 * row(1, 2, 16384, 128)   # few heads: split
+    assert f(1, 32, 8192, 128, 1, 0) == 0                            # grid already full
+    assert f(1, 4, 256, 128, 1, 0) == 0                              # one 256-key unit
+    assert f(1, 8, 4096, 64, 1, 4) == 4 * row(1, 8, 4096, 64)
+    assert f(1, 8, 4096, 64, 1, 3) == 3 * row(1, 8, 4096, 64)        # 16 units -> 6,6,4
+    assert f(1, 1, 1000, 128, 0, 16) == 4 * row(1, 1, 1000, 128)     # capped by 4 units
+    assert f(1, 1, 100, 128, 1, 1) == 0
+    assert f(1, 32, 512, 128, 1, 0) == 0                             # short: no split
+    assert f(1, 8, 4096, 128, 0, 0) == 2 * row(1, 8, 4096, 128)      # 128 WGs -> 2 segments
+    for bad in [(1, 1, 100, 96, 1, 0), (1, 1, 100, 128, 1, 65), (1, 1, 100, 128, 1, -1),
+                (0, 1, 100, 128, 1, 0), (1, 1, 0, 128, 1, 0)]:
+        assert f(*bad) == -1, bad
+
+
+WS = BASE + 512 * MB
+
+
+def call_split(q=BASE, k=BASE + 64 * MB, v=BASE + 128 * MB, o=BASE + 192 * MB,
+               lse=BASE + 320 * MB, B=1, H=2, Hkv=2, N=4096, D=128, causal=1, dtype=0,
+               splits=4, ws=WS, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = osc.attn_fwd_splitkv_workspace(B, H, N, D, causal, splits)
+    return osc.load().attn_fwd_splitkv(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, splits,
+                                       ws, ws_bytes, None)
+
+
+def test_splitkv_rejections():
+    need = osc.attn_fwd_splitkv_workspace(1, 2, 4096, 128, 1, 4)
+    assert need > 0
+    assert call_split(splits=65) == 2
+    assert call_split(splits=-1) == 2
+    assert call_split(Hkv=3) == 2
+    assert call_split(D=96) == 3
+    assert call_split(ws=None) == 1
+    assert call_split(ws=WS + 8) == 4
+    assert call_split(ws_bytes=need - 1) == 7
+    assert call_split(ws=BASE + 64 * MB + 4096) == 6       # inside K
+    assert call_split(ws=BASE + 192 * MB - 256) == 6       # runs into O
+    assert call_split(q=None) == 1
+    assert osc.attn_status_str(7) != "unknown status"
+
+
 def call_softmax(x=BASE, y=BASE + 64 * MB, M=4, N=100):
     return osc.load().row_softmax(x, y, M, N, None)
 

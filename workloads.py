@@ -91,6 +91,12 @@ GQA = {
     "G2": AttnWorkload("G2", 2, 8, 1000, 64, False, "bf16", 2.0, 1.0, 51, Hkv=1),
 }
 
+# Long sequence, few heads: the case the FA page (section 7) splits along the
+# keys for; without a split the grid covers one CU per query tile.
+SPLITKV = {
+    "S1": AttnWorkload("S1", 1, 2, 16384, 128, True, "f16", 1.0, 1.0, 52),
+}
+
 SOFTMAX = {
     "R1": SoftmaxWorkload("R1", 1025, 257, 80.0, 48),
     "R2": SoftmaxWorkload("R2", 8192, 32768, 80.0, 49),
