@@ -124,7 +124,7 @@ attn_status_t attn_fwd_gqa(const void *q, const void *k, const void *v, float *o
  * second kernel then merges the segments of each row with
  * m = max_s m_s, l = sum_s l_s e^(m_s - m), O = sum_s o_s e^(m_s - m) / l
  * ("CUDA KV Cache: paged storage and long-context decode" (chengzipai.xyz),
- * section 7; FA page, section 7: split along K for long sequences with few
+ * section 6.4; FA page, section 7: split along K for long sequences with few
  * heads).  The result is the attn_fwd_gqa result up to rounding.  Both
  * kernels are enqueued on `stream`.
  *
@@ -153,6 +153,70 @@ attn_status_t attn_fwd_splitkv(const void *q, const void *k, const void *v, floa
  */
 int64_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t D, int causal,
                                    int num_splits);
+
+/* Largest segment count paged_decode accepts. */
+#define PAGED_MAX_SPLITS 4096
+
+/*
+ * paged_decode - one decode step of grouped-query attention over a paged
+ * key/value cache: for each request b and query head h,
+ *     o[b,h] = sum_{t < len_b} p_t v_t,  p = softmax over t of q[b,h] . k_t / sqrt(D),
+ *     lse[b,h] = ln sum_{t < len_b} exp(q[b,h] . k_t / sqrt(D)),
+ * where k_t, v_t are the cached key and value of logical token t of request b
+ * for K/V head floor(h / (Hq / Hkv)).  Definition and layout: "CUDA KV Cache:
+ * paged storage and long-context decode" (chengzipai.xyz), section 2 (cache
+ * [P][2][T][Hkv][D]; logical token t lives in physical page
+ * block_table[b][t / T] at offset t mod T), section 3 (the query head group
+ * shares its K/V head; the translation happens inside the kernel, nothing is
+ * gathered or copied) and section 5 (online softmax over the tokens).  The
+ * query is the request's newest token, so every cached token is visible.
+ *
+ *   q            [B, Hq, D] of `dtype`, 16-byte aligned.
+ *   cache        [P, 2, T, Hkv, D] of `dtype`, 16-byte aligned: page p, K (0)
+ *                or V (1), token slot, K/V head, dim; element
+ *                (((p*2 + kind)*T + slot)*Hkv + head)*D + d.
+ *   block_table  [B, max_pages] int32 (device), 4-byte aligned: entry
+ *                (b, i) is the physical page of request b's logical page i.
+ *                Only the pages holding tokens < len_b are read; each must
+ *                be in [0, P).
+ *   lengths      [B] int32 (device), 4-byte aligned: tokens of request b,
+ *                1 <= len_b <= max_pages * T.
+ *   o            [B, Hq, D] FP32 output, 16-byte aligned.
+ *   lse          [B, Hq] FP32 output (natural log), 4-byte aligned.
+ *   B, Hq, Hkv   requests, query heads, K/V heads: Hq % Hkv == 0 (else
+ *                ATTN_ERR_SHAPE) and Hq / Hkv <= 32 (else ATTN_ERR_UNSUPPORTED).
+ *   D            64 or 128 (else ATTN_ERR_UNSUPPORTED).
+ *   page_size    T, a power of two up to 65536 (else ATTN_ERR_UNSUPPORTED).
+ *   num_pages    P, pages in the cache.   max_pages  columns of block_table.
+ *   dtype        ATTN_F16 or ATTN_BF16 (q and cache).
+ *   num_splits   0: the library chooses; 1..PAGED_MAX_SPLITS: split each
+ *                request's token range [0, max_pages*T) into about that many
+ *                segments (KV page, section 6.4), merged as in
+ *                attn_fwd_splitkv.  A segment holds at most 2048 tokens, so
+ *                long ranges may get more.  Other values: ATTN_ERR_SHAPE.
+ *   workspace, workspace_bytes  as for attn_fwd_splitkv, sized by
+ *                paged_decode_workspace(...); NULL allowed when that is 0.
+ *   stream       HIP stream to enqueue on.
+ *
+ * lengths and block_table are device data, which the call does not read:
+ * a request whose length is out of range, or which uses a page id out of
+ * range, gets NaN in all of its o and lse entries (no out-of-range address is
+ * read).  Limits: P*2*T*Hkv*D < 2^62, max_pages*T < 2^31, B*max_pages < 2^31.
+ * o, lse and the workspace must not overlap the inputs or each other.
+ */
+attn_status_t paged_decode(const void *q, const void *cache, const int32_t *block_table,
+                           const int32_t *lengths, float *o, float *lse, int64_t B, int64_t Hq,
+                           int64_t Hkv, int64_t D, int64_t page_size, int64_t num_pages,
+                           int64_t max_pages, attn_dtype_t dtype, int num_splits, void *workspace,
+                           int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_decode_workspace - bytes of workspace paged_decode needs for these
+ * sizes (0 if it uses one segment), or -1 if they are invalid.  Pure host
+ * computation; enqueues nothing.
+ */
+int64_t paged_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                               int64_t max_pages, int num_splits);
 
 /*
  * row_softmax - y[r, :] = softmax(x[r, :]) for r < M.

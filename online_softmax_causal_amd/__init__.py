@@ -13,6 +13,10 @@ The entry points mirror the C ABI in ``include/osc_attn.h``:
     attn_fwd_splitkv(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, num_splits,
                      workspace, workspace_bytes, stream=None)
     attn_fwd_splitkv_workspace(B, H, N, D, causal, num_splits=0)
+    paged_decode(q, cache, block_table, lengths, o, lse, B, Hq, Hkv, D, page_size,
+                 num_pages, max_pages, dtype, num_splits, workspace, workspace_bytes,
+                 stream=None)
+    paged_decode_workspace(B, Hq, Hkv, D, page_size, max_pages, num_splits=0)
     attn_status_str(status)
 
 Pointer arguments accept device tensors (``torch.Tensor``, only its address is
@@ -42,7 +46,7 @@ STATUS = {
     7: "ATTN_ERR_WORKSPACE",
 }
 EXPORTS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace",
-           "row_softmax", "attn_status_str")
+           "paged_decode", "paged_decode_workspace", "row_softmax", "attn_status_str")
 
 _lib = None
 
@@ -74,6 +78,11 @@ def load():
     lib.attn_fwd_splitkv.restype = ctypes.c_int
     lib.attn_fwd_splitkv_workspace.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.attn_fwd_splitkv_workspace.restype = i64
+    lib.paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                 ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    lib.paged_decode.restype = ctypes.c_int
+    lib.paged_decode_workspace.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.paged_decode_workspace.restype = i64
     lib.row_softmax.argtypes = [vp, vp, i64, i64, vp]
     lib.row_softmax.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
@@ -149,6 +158,23 @@ def attn_fwd_splitkv(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, num_splits
                                  _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_fwd_splitkv")
+
+
+def paged_decode_workspace(B, Hq, Hkv, D, page_size, max_pages, num_splits=0) -> int:
+    """Workspace bytes paged_decode needs (0: one segment, no workspace); -1 if invalid."""
+    return int(load().paged_decode_workspace(int(B), int(Hq), int(Hkv), int(D), int(page_size),
+                                             int(max_pages), int(num_splits)))
+
+
+def paged_decode(q, cache, block_table, lengths, o, lse, B, Hq, Hkv, D, page_size, num_pages,
+                 max_pages, dtype, num_splits, workspace, workspace_bytes, stream=None) -> None:
+    """Enqueue one paged grouped-query decode step (block_table, lengths: int32 device)."""
+    st = load().paged_decode(_ptr(q), _ptr(cache), _ptr(block_table), _ptr(lengths), _ptr(o),
+                             _ptr(lse), int(B), int(Hq), int(Hkv), int(D), int(page_size),
+                             int(num_pages), int(max_pages), _dtype(dtype), int(num_splits),
+                             _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "paged_decode")
 
 
 def row_softmax(x, y, M, N, stream=None) -> None:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libosc_attn.so")
-SOURCES = ["attn_fwd.hip", "splitkv.hip", "row_softmax.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "decode.hip", "splitkv.hip", "row_softmax.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -36,9 +36,9 @@ def _compile(src: str) -> str:
     return obj
 
 
-def check_m0(src: str = "attn_fwd.hip") -> None:
-    """The attention kernel writes M0 in inline assembly (the LDS address of
-    global_load_lds_dwordx4).  That is only safe while no compiler-generated
+def check_m0(src: str) -> None:
+    """The attention and decode kernels write M0 in inline assembly (the LDS
+    address of global_load_lds_dwordx4).  That is only safe while no compiler-generated
     instruction uses M0, so check the generated gfx950 assembly: every M0
     reference must be one of those writes, directly followed by the copy."""
     asm = os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
@@ -59,10 +59,11 @@ def check_m0(src: str = "attn_fwd.hip") -> None:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
-        m0 = ex.submit(check_m0)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
+        m0 = [ex.submit(check_m0, src) for src in ("attn_fwd.hip", "decode.hip")]
         objs = list(ex.map(_compile, SOURCES))
-        m0.result()
+        for f in m0:
+            f.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -78,6 +78,66 @@ attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, float* o
     return attn_fwd_impl(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, stream);
 }
 
+// Decode split plan and workspace size for valid sizes; false if they are not.
+static bool paged_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                       int64_t num_pages, int64_t max_pages, int num_splits, attn_status_t* status,
+                       int* log2_page, osc::DecodePlan* plan, int64_t* bytes) {
+    if (!osc::paged_sizes_ok(B, Hq, Hkv, D, page_size, num_pages, max_pages, status, log2_page))
+        return false;
+    *status = ATTN_ERR_SHAPE;
+    if (num_splits < 0 || num_splits > PAGED_MAX_SPLITS) return false;
+    *plan = osc::paged_decode_plan(B, Hkv, max_pages * page_size, num_splits);
+    if (B * Hkv * plan->nseg >= (int64_t(1) << 31)) return false;
+    int64_t words = 0;
+    if (!osc::mul_below_2_62(B * Hq * (D + 2), plan->nseg, &words) || words >= (int64_t(1) << 60))
+        return false;
+    *bytes = plan->nseg > 1 ? words * 4 : 0;
+    return true;
+}
+
+int64_t paged_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                               int64_t max_pages, int num_splits) {
+    attn_status_t st;
+    int lp = 0;
+    osc::DecodePlan plan;
+    int64_t bytes = 0;
+    // The cache size does not enter the plan; one page stands in for it.
+    return paged_plan(B, Hq, Hkv, D, page_size, 1, max_pages, num_splits, &st, &lp, &plan, &bytes)
+               ? bytes
+               : -1;
+}
+
+attn_status_t paged_decode(const void* q, const void* cache, const int32_t* block_table,
+                           const int32_t* lengths, float* o, float* lse, int64_t B, int64_t Hq,
+                           int64_t Hkv, int64_t D, int64_t page_size, int64_t num_pages,
+                           int64_t max_pages, attn_dtype_t dtype, int num_splits, void* workspace,
+                           int64_t workspace_bytes, hipStream_t stream) {
+    attn_status_t st = ATTN_OK;
+    int lp = 0;
+    osc::DecodePlan plan;
+    int64_t need = 0;
+    if (!paged_plan(B, Hq, Hkv, D, page_size, num_pages, max_pages, num_splits, &st, &lp, &plan,
+                    &need)) {
+        // A null pointer is reported before a size problem, as for attention.
+        if (!q || !cache || !block_table || !lengths || !o || !lse) return ATTN_ERR_NULL;
+        return st;
+    }
+    st = osc::validate_paged(q, cache, block_table, lengths, o, lse, B, Hq, Hkv, D, page_size,
+                             num_pages, max_pages, dtype);
+    if (st != ATTN_OK) return st;
+    st = osc::validate_paged_workspace(workspace, workspace_bytes, need, q, cache, block_table,
+                                       lengths, o, lse, B, Hq, Hkv, D, page_size, num_pages,
+                                       max_pages);
+    if (st != ATTN_OK) return st;
+    float* part_o = static_cast<float*>(workspace);
+    float2* part_ml =
+        plan.nseg > 1 ? reinterpret_cast<float2*>(part_o + (int64_t)plan.nseg * B * Hq * D) : nullptr;
+    const hipError_t e = osc::launch_paged_decode(
+        q, cache, block_table, lengths, o, lse, (int)B, (int)Hq, (int)Hkv, (int)D, lp,
+        (int)num_pages, (int)max_pages, dtype == ATTN_BF16, plan, part_o, part_ml, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 attn_status_t row_softmax(const float* x, float* y, int64_t M, int64_t N, hipStream_t stream) {
     const attn_status_t st = osc::validate_softmax(x, y, M, N);
     if (st != ATTN_OK) return st;

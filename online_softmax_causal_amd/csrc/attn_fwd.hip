@@ -37,68 +37,11 @@
 #include <cstdint>
 
 #include "kernels.hpp"
+#include "mfma_tile.hpp"
 #include "online_merge.hpp"
 
 namespace osc {
 namespace {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16;
-
-template <bool BF16>
-struct Mma;
-
-// kSumRounded: whether the row sum l is taken over the 16-bit P fed to the
-// P V product (fp16: rounding error <= 2^-11 relative, so numerator and
-// denominator stay consistent and the LSE error stays below 5e-4) or over the
-// FP32 P before rounding (bf16: its 2^-9 rounding would move the LSE by up to
-// 2e-3 on rows dominated by one key).
-template <>
-struct Mma<false> {
-    static constexpr bool kSumRounded = true;
-    __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-    // Round-to-nearest-even conversion of two FP32 values into one packed dword.
-    __device__ __forceinline__ static unsigned pack(float lo, float hi) {
-        f16x2 r;
-        r[0] = (_Float16)lo;
-        r[1] = (_Float16)hi;
-        return __builtin_bit_cast(unsigned, r);
-    }
-    // acc + lo + hi of one packed dword, accumulated in FP32.
-    __device__ __forceinline__ static float sum2(unsigned packed, float acc) {
-        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
-    }
-};
-
-template <>
-struct Mma<true> {
-    static constexpr bool kSumRounded = false;
-    __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-    __device__ __forceinline__ static unsigned pack(float lo, float hi) {
-        bf16x2 r;
-        r[0] = (__bf16)lo;
-        r[1] = (__bf16)hi;
-        return __builtin_bit_cast(unsigned, r);
-    }
-    __device__ __forceinline__ static float sum2(unsigned packed, float acc) {
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
-    }
-};
 
 // Compile-time geometry of one kernel instance.
 //
@@ -132,14 +75,6 @@ struct Geo {
     static_assert(DIST == 1 || DIST == 2, "prefetch distance");
 };
 
-template <int D>
-__device__ __forceinline__ int chunk_swizzle(int r) {
-    if constexpr (D == 128)
-        return ((r & 3) << 2) | ((r >> 2) & 3);
-    else
-        return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
 // Kernel arguments (one struct, passed by value).
 struct AttnArgs {
     const u16* q;   // [B, H, N, D]
@@ -170,22 +105,6 @@ struct WaveState {
     float m[QB];              // reference max of this lane's query, log2 units
     float l[QB];              // this lane's share of the running sum (relative to m)
 };
-
-// Conditional rescaling: the reference max m moves only when a query's
-// tile max exceeds it by more than 2^8.  Between moves the exponentials are
-// taken against a stale m, so each P element is at most 2^8 (exact in fp16
-// and bf16 range); O and l always share the same reference, so O = o/l is
-// unchanged.  This skips the rescale of the O accumulator on most tiles.
-constexpr float kRescaleSlack = 8.0f;
-
-__device__ __forceinline__ u32x4 tr16_b64x2(const u16* p0, const u16* p1) {
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
-    const auto a = __builtin_bit_cast(unsigned long long, r0);
-    const auto b = __builtin_bit_cast(unsigned long long, r1);
-    return u32x4{(unsigned)a, (unsigned)(a >> 32), (unsigned)b, (unsigned)(b >> 32)};
-}
 
 // Per-lane LDS offsets (16-bit elements, relative to a tile) of the MFMA
 // operand fragments, swizzle included; fixed for the whole kernel.
@@ -221,8 +140,9 @@ __device__ __forceinline__ FragOffsets<G::D> frag_offsets(int lane) {
 // S^T[key][query] = sum_d K[key][d] Q[query][d] for the 64 keys of one K
 // tile (two 32-key accumulators per query block).  The 2*KS A-operand
 // fragments stream through a 4-deep register ring so each LDS read is issued
-// four fragments ahead of its use; each fragment feeds the MFMAs of all QB
-// query blocks, and consecutive MFMAs alternate accumulators.
+// four fragments ahead of its use (enforced with scheduling groups); each
+// fragment feeds the MFMAs of all QB query blocks, and consecutive MFMAs
+// alternate accumulators.
 template <bool BF16, class G, int QB>
 __device__ __forceinline__ void qk_tile(const WaveState<G::D, QB>& st, const FragOffsets<G::D>& fo,
                                         const u16* kt, f32x16 (&s)[QB][2]) {
@@ -231,6 +151,7 @@ __device__ __forceinline__ void qk_tile(const WaveState<G::D, QB>& st, const Fra
     auto kfrag = [&](int f) {
         return *reinterpret_cast<const u32x4*>(kt + fo.k[f >> 1] + (f & 1) * 32 * G::D);
     };
+    __builtin_amdgcn_sched_barrier(0);
     u32x4 ring[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) ring[f] = kfrag(f);
@@ -246,6 +167,16 @@ __device__ __forceinline__ void qk_tile(const WaveState<G::D, QB>& st, const Fra
 #pragma unroll
         for (int b = 0; b < QB; ++b) s[b][f & 1] = M::run(a, st.qf[b][f >> 1], s[b][f & 1]);
     }
+    // Keep the ring: without these groups the scheduler, tight on registers,
+    // issued each read right before its MFMA and waited for it there.
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+#pragma unroll
+    for (int f = 0; f < NF - 4; ++f) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, QB, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 4 * QB, 0);
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Online-softmax update and O^T += V^T P^T for one 64-key tile whose raw
@@ -358,23 +289,6 @@ __device__ __forceinline__ void softmax_pv_tile(WaveState<G::D, QB>& st, const F
     }
 }
 
-// Byte offset of an LDS location (what M0 and ds_* addresses use).
-__device__ __forceinline__ unsigned lds_offset(const void* p) {
-    return (unsigned)(unsigned long long)((const __attribute__((address_space(3))) char*)p);
-}
-
-// global_load_lds_dwordx4: each lane copies 16 bytes from gbase + voff to
-// LDS address m0 + 16 * lane.  Written as inline assembly so the compiler's
-// memory model does not see an LDS store: it would otherwise make every
-// later LDS read wait for the copy, which targets a stage that no wave reads
-// until the barrier after the matching wait_vmcnt.
-__device__ __forceinline__ void copy_to_lds16(const void* gbase, unsigned voff, void* lds_dst) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds_offset(lds_dst)), "v"(voff), "s"(gbase)
-                 : "m0");
-}
-
 // Issue the direct global->LDS copy of rows [tile*BC, tile*BC + BC) of one
 // head's K (or V) into an LDS tile.  Rows past N are clamped to row N-1: they
 // only feed keys that are masked (score -inf, weight exactly 0).
@@ -390,15 +304,6 @@ __device__ __forceinline__ void dma_tile(const u16* __restrict__ src, u16* dst, 
         const int key = min(tile * G::BC + r, N - 1);
         copy_to_lds16(src, (unsigned)((key * D + c * 8) * 2), dst + blk * 512);
     }
-}
-
-// Wait until at most `n` of this wave's vector-memory loads are outstanding
-// (gfx9 s_waitcnt encoding: vmcnt low bits [3:0], expcnt and lgkmcnt left at
-// their maxima so they are not waited on).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(n >= 0 && n < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | n);
 }
 
 // NW waves of 32 query rows; MINWG workgroups must fit on one CU at once
@@ -710,7 +615,7 @@ hipError_t launch_attn_fwd(const void* q, const void* k, const void* v, float* o
                                 stream);
 }
 
-// Split-KV plan (KV page, section 7: split the keys when the query side
+// Split-KV plan (KV page, section 6.4: split the keys when the query side
 // alone cannot fill the chip; the count depends on B*H, length and the
 // number of CUs).  `requested` > 0 asks for that many segments.  With 0 the
 // plan keeps one segment when the plain grid has two workgroups per CU or N

@@ -40,6 +40,29 @@ hipError_t launch_splitkv_merge(const float* part_o, const float2* part_ml, floa
                                 int BH, int N, int D, int nseg, int seg_rows, bool causal,
                                 hipStream_t stream);
 
+// Paged decode: tokens per tile, and the most tokens one segment may hold
+// (its page ids are staged in LDS, one slot per page).
+constexpr int kDecTile = 32;
+constexpr int kDecMaxSegTokens = 2048;
+
+// Split of every request's token range [0, max_pages * T) into nseg segments
+// of seg_tokens tokens (a multiple of kDecTile).
+struct DecodePlan {
+    int nseg;
+    int seg_tokens;
+};
+
+// requested = 0 chooses automatically; cap = max_pages * T.
+DecodePlan paged_decode_plan(int64_t B, int64_t Hkv, int64_t cap, int requested);
+
+// With plan.nseg > 1, part_o [nseg, B*Hq, D] and part_ml [nseg, B*Hq] receive
+// the segments' states and the split-KV merge kernel combines them.
+hipError_t launch_paged_decode(const void* q, const void* cache, const int* block_table,
+                               const int* lengths, float* o, float* lse, int B, int Hq, int Hkv,
+                               int D, int log2_page, int P, int max_pages, bool bf16,
+                               const DecodePlan& plan, float* part_o, float2* part_ml,
+                               hipStream_t stream);
+
 hipError_t launch_row_softmax(const float* x, float* y, int64_t M, int64_t N, hipStream_t stream);
 
 }  // namespace osc

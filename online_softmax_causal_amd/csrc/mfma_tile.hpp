@@ -1,0 +1,135 @@
+// MFMA operand helpers shared by the attention kernels (gfx950, wave64):
+// 16-bit vector types, the 32x32x16 MFMA with its 16-bit packing and pair
+// sums, the LDS chunk swizzle, LDS transpose reads, direct global->LDS copies
+// and explicit vector-memory waits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace osc {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+template <bool BF16>
+struct Mma;
+
+// kSumRounded: whether the row sum l is taken over the 16-bit P fed to the
+// P V product (fp16: rounding error <= 2^-11 relative, so numerator and
+// denominator stay consistent and the LSE error stays below 5e-4) or over the
+// FP32 P before rounding (bf16: its 2^-9 rounding would move the LSE by up to
+// 2e-3 on rows dominated by one key).
+template <>
+struct Mma<false> {
+    static constexpr bool kSumRounded = true;
+    __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    // Round-to-nearest-even conversion of two FP32 values into one packed dword.
+    __device__ __forceinline__ static unsigned pack(float lo, float hi) {
+        f16x2 r;
+        r[0] = (_Float16)lo;
+        r[1] = (_Float16)hi;
+        return __builtin_bit_cast(unsigned, r);
+    }
+    // acc + lo + hi of one packed dword, accumulated in FP32.
+    __device__ __forceinline__ static float sum2(unsigned packed, float acc) {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
+    }
+};
+
+template <>
+struct Mma<true> {
+    static constexpr bool kSumRounded = false;
+    __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static unsigned pack(float lo, float hi) {
+        bf16x2 r;
+        r[0] = (__bf16)lo;
+        r[1] = (__bf16)hi;
+        return __builtin_bit_cast(unsigned, r);
+    }
+    __device__ __forceinline__ static float sum2(unsigned packed, float acc) {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+    }
+};
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008;
+constexpr int kSgDsRead = 0x100;
+
+template <int D>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+    if constexpr (D == 128)
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    else
+        return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Conditional rescaling: the reference max m moves only when a query's
+// tile max exceeds it by more than 2^8.  Between moves the exponentials are
+// taken against a stale m, so each P element is at most 2^8 (exact in fp16
+// and bf16 range); O and l always share the same reference, so O = o/l is
+// unchanged.  This skips the rescale of the O accumulator on most tiles.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ u32x4 tr16_b64x2(const u16* p0, const u16* p1) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+    const auto a = __builtin_bit_cast(unsigned long long, r0);
+    const auto b = __builtin_bit_cast(unsigned long long, r1);
+    return u32x4{(unsigned)a, (unsigned)(a >> 32), (unsigned)b, (unsigned)(b >> 32)};
+}
+
+// Byte offset of an LDS location (what M0 and ds_* addresses use).
+__device__ __forceinline__ unsigned lds_offset(const void* p) {
+    return (unsigned)(unsigned long long)((const __attribute__((address_space(3))) char*)p);
+}
+
+// global_load_lds_dwordx4: each lane copies 16 bytes from gbase + voff to
+// LDS address m0 + 16 * lane.  Written as inline assembly so the compiler's
+// memory model does not see an LDS store: it would otherwise make every
+// later LDS read wait for the copy, which targets a stage that no wave reads
+// until the barrier after the matching wait_vmcnt.
+__device__ __forceinline__ void copy_to_lds16(const void* gbase, unsigned voff, void* lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_offset(lds_dst)), "v"(voff), "s"(gbase)
+                 : "m0");
+}
+
+// The same copy from a full 64-bit global address per lane (gathers whose
+// offsets do not fit 32 bits, e.g. rows of a paged cache).
+__device__ __forceinline__ void copy_to_lds16_at(const void* gaddr, void* lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_offset(lds_dst)), "v"(gaddr)
+                 : "m0");
+}
+
+// Wait until at most `n` of this wave's vector-memory loads are outstanding
+// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt are left at their maxima so they
+// are not waited on).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt field");
+    // vmcnt is split: bits [3:0] hold its low four bits, bits [15:14] the high two.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
+}  // namespace osc

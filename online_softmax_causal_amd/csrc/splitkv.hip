@@ -5,7 +5,7 @@
 // its scaled logits in base-2 units, l_s = sum_j 2^(x_j - m_s) and
 // o_s = sum_j 2^(x_j - m_s) v_j over the segment's visible keys.  The row's
 // result follows the split-KV merge of "CUDA KV Cache: paged storage and
-// long-context decode" (chengzipai.xyz), section 7:
+// long-context decode" (chengzipai.xyz), section 6.4:
 //     m = max_s m_s,  l = sum_s l_s 2^(m_s - m),  O = sum_s o_s 2^(m_s - m) / l,
 // the same law as the tile recurrence (FA page, section 4), folded here one
 // segment at a time with the shared online_rescale.  LSE = (m + log2 l) ln 2.

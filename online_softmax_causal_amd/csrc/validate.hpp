@@ -72,6 +72,80 @@ inline attn_status_t validate_workspace(const void* ws, int64_t ws_bytes, int64_
     return ATTN_OK;
 }
 
+// Sizes of a paged decode call: false if they are invalid (a size < 1, Hkv
+// not dividing Hq, or a product past the limits); *status then says which
+// code to return.  Sets *log2_page for valid sizes.
+inline bool paged_sizes_ok(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                           int64_t num_pages, int64_t max_pages, attn_status_t* status,
+                           int* log2_page) {
+    *status = ATTN_ERR_SHAPE;
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || page_size < 1 || num_pages < 1 || max_pages < 1)
+        return false;
+    if (Hq % Hkv != 0) return false;
+    *status = ATTN_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return false;
+    if (Hq / Hkv > 32) return false;
+    if (page_size > 65536 || (page_size & (page_size - 1)) != 0) return false;
+    int lp = 0;
+    while ((int64_t(1) << lp) < page_size) ++lp;
+    *log2_page = lp;
+    *status = ATTN_ERR_SHAPE;
+    int64_t rows = 0, elems = 0, cap = 0, bt = 0, bq = 0, bqd = 0;
+    if (!mul_below_2_62(num_pages * 2, page_size, &rows) || !mul_below_2_62(rows, Hkv, &rows) ||
+        !mul_below_2_62(rows, D, &elems))
+        return false;
+    if (!mul_below_2_62(max_pages, page_size, &cap) || cap >= (int64_t(1) << 31)) return false;
+    if (!mul_below_2_62(B, max_pages, &bt) || bt >= (int64_t(1) << 31)) return false;
+    if (!mul_below_2_62(B, Hq, &bq) || !mul_below_2_62(bq, D, &bqd) || bq >= (int64_t(1) << 31))
+        return false;
+    if (num_pages >= (int64_t(1) << 31)) return false;
+    return true;
+}
+
+// Pointers of a paged decode call whose sizes passed paged_sizes_ok.
+inline attn_status_t validate_paged(const void* q, const void* cache, const int32_t* block_table,
+                                    const int32_t* lengths, const float* o, const float* lse,
+                                    int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                    int64_t page_size, int64_t num_pages, int64_t max_pages,
+                                    attn_dtype_t dtype) {
+    if (!q || !cache || !block_table || !lengths || !o || !lse) return ATTN_ERR_NULL;
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(o, 16) || !aligned(block_table, 4) ||
+        !aligned(lengths, 4) || !aligned(lse, 4))
+        return ATTN_ERR_ALIGN;
+    const int64_t q_bytes = B * Hq * D * 2;
+    const int64_t cache_bytes = num_pages * 2 * page_size * Hkv * D * 2;
+    const int64_t bt_bytes = B * max_pages * 4, len_bytes = B * 4;
+    const int64_t o_bytes = B * Hq * D * 4, lse_bytes = B * Hq * 4;
+    const void* ins[4] = {q, cache, block_table, lengths};
+    const int64_t in_bytes[4] = {q_bytes, cache_bytes, bt_bytes, len_bytes};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(o, o_bytes, ins[i], in_bytes[i]) || overlap(lse, lse_bytes, ins[i], in_bytes[i]))
+            return ATTN_ERR_ALIAS;
+    if (overlap(o, o_bytes, lse, lse_bytes)) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+// Workspace of a paged decode call that needs `need` bytes (0: none is used).
+inline attn_status_t validate_paged_workspace(const void* ws, int64_t ws_bytes, int64_t need,
+                                              const void* q, const void* cache,
+                                              const int32_t* block_table, const int32_t* lengths,
+                                              const float* o, const float* lse, int64_t B,
+                                              int64_t Hq, int64_t Hkv, int64_t D,
+                                              int64_t page_size, int64_t num_pages,
+                                              int64_t max_pages) {
+    if (need == 0) return ATTN_OK;
+    if (!ws) return ATTN_ERR_NULL;
+    if (!aligned(ws, 16)) return ATTN_ERR_ALIGN;
+    if (ws_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (overlap(ws, need, q, B * Hq * D * 2) ||
+        overlap(ws, need, cache, num_pages * 2 * page_size * Hkv * D * 2) ||
+        overlap(ws, need, block_table, B * max_pages * 4) || overlap(ws, need, lengths, B * 4) ||
+        overlap(ws, need, o, B * Hq * D * 4) || overlap(ws, need, lse, B * Hq * 4))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
 inline attn_status_t validate_softmax(const float* x, const float* y, int64_t M, int64_t N) {
     if (!x || !y) return ATTN_ERR_NULL;
     if (M < 1 || N < 1) return ATTN_ERR_SHAPE;

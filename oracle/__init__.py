@@ -15,7 +15,10 @@ statement):
   limits" (chengzipai.xyz), section 1 (O = softmax(QK^T/sqrt(D) + M)V, causal
   mask j <= i) and section 3 (the naive three stages);
 * row softmax: the softmax kernel study (lpnh.cn/news/2830604), section 3.1
-  (double-precision stable softmax as the CPU reference).
+  (double-precision stable softmax as the CPU reference);
+* paged decode: "CUDA KV Cache: paged storage and long-context decode"
+  (chengzipai.xyz), sections 2 (page-table addressing), 3 (query-head groups
+  share a K/V head) and 5 (attention of the new token over the cached ones).
 
 Pins: every function here is checked in ``tests/test_oracle.py`` against
 closed forms, invariants and independent library routines.
@@ -56,6 +59,12 @@ def _bind(path: str):
     lib.oracle_attn_fwd.argtypes = [_PD, _PD, _PD, _PD, _PD, _I64, _I64, _I64, _I64,
                                     ctypes.c_int, ctypes.c_int]
     lib.oracle_attn_fwd.restype = ctypes.c_int
+    lib.oracle_paged_decode.argtypes = [_PD, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                        _PI64, _I64, _PD, _PD, ctypes.c_int]
+    lib.oracle_paged_decode.restype = ctypes.c_int
+    lib.oracle_bits_to_double.argtypes = [ctypes.c_void_p, ctypes.c_int, _I64, _PD]
+    lib.oracle_bits_to_double.restype = ctypes.c_int
     lib.oracle_attn_rows.argtypes = [_PD, _PD, _PD, _I64, _I64, _I64, _I64, ctypes.c_int,
                                      _PI64, _I64, _PD, _PD, ctypes.c_int]
     lib.oracle_attn_rows.restype = ctypes.c_int
@@ -197,6 +206,65 @@ def attn_scores(q, k, causal: bool, i: int) -> np.ndarray:
     if n < 0:
         raise RuntimeError("oracle_attn_scores failed")
     return s[:n].copy()
+
+
+# -------------------------------------------------------------- paged decode
+
+def _bits16(a):
+    """(uint16 bits, is_bf16) of a CPU torch fp16/bf16 tensor or a numpy float16 array."""
+    if hasattr(a, "detach"):
+        import torch
+        t = a.detach().contiguous()
+        if t.dtype not in (torch.float16, torch.bfloat16):
+            raise TypeError("the cache must be fp16 or bf16")
+        return np.ascontiguousarray(t.view(torch.int16).numpy().view(np.uint16)), \
+            int(t.dtype == torch.bfloat16)
+    a = np.ascontiguousarray(np.asarray(a))
+    if a.dtype != np.float16:
+        raise TypeError("the cache must be fp16 or bf16")
+    return a.view(np.uint16), 0
+
+
+def bits_to_f64(a) -> np.ndarray:
+    """The cache converter used by paged_decode (exact decoding in oracle.c)."""
+    bits, is_bf16 = _bits16(a)
+    out = np.empty(bits.shape, np.float64)
+    if _load().oracle_bits_to_double(bits.ctypes.data, is_bf16, bits.size, _ptr(out)) != 0:
+        raise RuntimeError("oracle_bits_to_double failed")
+    return out
+
+
+def paged_decode(q, cache, block_table, lengths, page_size: int, rows=None,
+                 nthreads: int | None = None):
+    """Paged grouped-query decode in float64.
+
+    q [B, Hq, D] (any float type), cache [P, 2, T, Hkv, D] fp16/bf16 (CPU),
+    block_table [B, max_pages] and lengths [B] integers.  rows: flat ids
+    b*Hq + h to compute (all if None).  Returns o [len(rows), D] and
+    lse [len(rows)]; invalid requests get NaN.
+    """
+    qd = to_f64(q)
+    B, Hq, D = qd.shape
+    bits, is_bf16 = _bits16(cache)
+    P, two, T, Hkv, Dc = bits.shape
+    if two != 2 or T != page_size or Dc != D:
+        raise ValueError("cache must be [P, 2, page_size, Hkv, D]")
+    bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    ln = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    if bt.ndim != 2 or bt.shape[0] != B or ln.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and lengths [B]")
+    if rows is None:
+        rows = np.arange(B * Hq)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    o = np.empty((rows.size, D), np.float64)
+    lse = np.empty((rows.size,), np.float64)
+    rc = _load().oracle_paged_decode(_ptr(qd), bits.ctypes.data, is_bf16, bt.ctypes.data,
+                                     ln.ctypes.data, B, Hq, Hkv, D, T, P, bt.shape[1],
+                                     rows.ctypes.data_as(_PI64), rows.size, _ptr(o), _ptr(lse),
+                                     nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_paged_decode failed (%d)" % rc)
+    return o, lse
 
 
 # --------------------------------------------------------------- row softmax

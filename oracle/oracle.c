@@ -21,6 +21,18 @@
  *   sum_j exp(s_ij) over the same keys (the page's section 7 only says the
  *   LSE is saved for the backward pass; this is the plain reading).
  *
+ *   Paged decode, from "CUDA KV Cache: paged storage and long-context
+ *   decode" (chengzipai.xyz), sections 2, 3 and 5: one query per (request b,
+ *   query head h) attends over the request's len_b cached tokens.  Token t of
+ *   request b is slot t mod T of physical page block_table[b][t / T] in the
+ *   cache [P][2][T][Hkv][D] (kind 0 = K, 1 = V), read for K/V head
+ *   floor(h / (Hq / Hkv)).  The three stages are those of attention, with every
+ *   cached token visible.  A request whose length is outside [1, max_pages*T]
+ *   or which uses a page id outside [0, P) gets NaN outputs (the convention of
+ *   the interface this oracle checks).  The cache arrives as raw fp16 or bf16
+ *   bits and each element is decoded exactly to double here (IEEE binary16
+ *   and bfloat16 formats).
+ *
  *   Row softmax, from the softmax kernel study (lpnh.cn/news/2830604),
  *   section 3.1: a double-precision stable softmax per row,
  *     m = max_j x_j, e_j = exp(x_j - m), d = sum_j e_j, y_j = e_j / d.
@@ -40,6 +52,7 @@
 #include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 /* ---------------------------------------------------------------- attention */
 
@@ -187,6 +200,167 @@ int64_t oracle_attn_scores(const double *q, const double *k, int64_t N, int64_t 
     if (!q || !k || !s || N < 1 || D < 1 || i < 0 || i >= N)
         return -1;
     return scores_row(q, k, N, D, causal, i, s);
+}
+
+/* ------------------------------------------------------------- paged decode */
+
+/* Exact value of a binary16 bit pattern. */
+static double half_bits_to_double(uint16_t h)
+{
+    const int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal or zero */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return sign ? -v : v;
+}
+
+/* Exact value of a bfloat16 bit pattern (the high half of a binary32). */
+static double bf16_bits_to_double(uint16_t h)
+{
+    const uint32_t w = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    const double *q;               /* [B, Hq, D] */
+    const uint16_t *cache;         /* [P, 2, T, Hkv, D] raw bits */
+    int is_bf16;
+    const int32_t *block_table;    /* [B, max_pages] */
+    const int32_t *lengths;        /* [B] */
+    double *o, *lse;               /* [nrows, D], [nrows] */
+    int64_t Hq, Hkv, D, T, P, max_pages;
+    const int64_t *rows;           /* flat ids b*Hq + h */
+    int64_t begin, end;
+    int status;
+} dec_job;
+
+static double cache_at(const dec_job *jb, int64_t page, int kind, int64_t slot, int64_t kvh,
+                       int64_t d)
+{
+    const int64_t idx = (((page * 2 + kind) * jb->T + slot) * jb->Hkv + kvh) * jb->D + d;
+    return jb->is_bf16 ? bf16_bits_to_double(jb->cache[idx]) : half_bits_to_double(jb->cache[idx]);
+}
+
+static void *dec_worker(void *arg)
+{
+    dec_job *jb = (dec_job *)arg;
+    const int64_t cap = jb->max_pages * jb->T;
+    double *s = (double *)malloc((size_t)cap * sizeof(double));
+    if (!s) {
+        jb->status = -2;
+        return NULL;
+    }
+    const double root_d = sqrt((double)jb->D);
+    for (int64_t r = jb->begin; r < jb->end; ++r) {
+        const int64_t flat = jb->rows[r];
+        const int64_t b = flat / jb->Hq, h = flat % jb->Hq;
+        const int64_t kvh = h / (jb->Hq / jb->Hkv);
+        const int64_t len = jb->lengths[b];
+        double *o_row = jb->o + r * jb->D;
+        int valid = len >= 1 && len <= cap;
+        for (int64_t t = 0; valid && t < len; t += jb->T) {
+            const int64_t page = jb->block_table[b * jb->max_pages + t / jb->T];
+            if (page < 0 || page >= jb->P)
+                valid = 0;
+        }
+        if (!valid) {
+            for (int64_t d = 0; d < jb->D; ++d)
+                o_row[d] = NAN;
+            jb->lse[r] = NAN;
+            continue;
+        }
+        /* stage 1: the score of every cached token */
+        const double *qr = jb->q + flat * jb->D;
+        for (int64_t t = 0; t < len; ++t) {
+            const int64_t page = jb->block_table[b * jb->max_pages + t / jb->T];
+            double dot = 0.0;
+            for (int64_t d = 0; d < jb->D; ++d)
+                dot += qr[d] * cache_at(jb, page, 0, t % jb->T, kvh, d);
+            s[t] = dot / root_d;
+        }
+        /* stage 2: safe softmax */
+        double m = s[0];
+        for (int64_t t = 1; t < len; ++t)
+            if (s[t] > m)
+                m = s[t];
+        double l = 0.0;
+        for (int64_t t = 0; t < len; ++t) {
+            s[t] = exp(s[t] - m);
+            l += s[t];
+        }
+        for (int64_t t = 0; t < len; ++t)
+            s[t] = s[t] / l;
+        /* stage 3: P times V */
+        for (int64_t d = 0; d < jb->D; ++d)
+            o_row[d] = 0.0;
+        for (int64_t t = 0; t < len; ++t) {
+            const int64_t page = jb->block_table[b * jb->max_pages + t / jb->T];
+            for (int64_t d = 0; d < jb->D; ++d)
+                o_row[d] += s[t] * cache_at(jb, page, 1, t % jb->T, kvh, d);
+        }
+        jb->lse[r] = m + log(l);
+    }
+    free(s);
+    jb->status = 0;
+    return NULL;
+}
+
+/* Selected (request, query head) pairs rows[r] = b*Hq + h; o_rows [nrows, D], lse_rows [nrows]. */
+int oracle_paged_decode(const double *q, const uint16_t *cache, int is_bf16,
+                        const int32_t *block_table, const int32_t *lengths, int64_t B, int64_t Hq,
+                        int64_t Hkv, int64_t D, int64_t T, int64_t P, int64_t max_pages,
+                        const int64_t *rows, int64_t nrows, double *o_rows, double *lse_rows,
+                        int nthreads)
+{
+    if (!q || !cache || !block_table || !lengths || !rows || !o_rows || !lse_rows || B < 1 ||
+        Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || T < 1 || P < 1 || max_pages < 1 || nrows < 0)
+        return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= B * Hq)
+            return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if ((int64_t)nthreads > nrows)
+        nthreads = nrows > 0 ? (int)nrows : 1;
+    dec_job jobs[256];
+    pthread_t tid[256];
+    int started[256] = {0};
+    for (int t = 0; t < nthreads; ++t) {
+        dec_job jb = {q, cache, is_bf16, block_table, lengths, o_rows, lse_rows, Hq, Hkv, D, T, P,
+                      max_pages, rows, nrows * t / nthreads, nrows * (t + 1) / nthreads, -2};
+        jobs[t] = jb;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        started[t] = pthread_create(&tid[t], NULL, dec_worker, &jobs[t]) == 0;
+    dec_worker(&jobs[0]);
+    int status = jobs[0].status;
+    for (int t = 1; t < nthreads; ++t) {
+        if (started[t])
+            pthread_join(tid[t], NULL);
+        else
+            dec_worker(&jobs[t]);
+        if (jobs[t].status != 0)
+            status = jobs[t].status;
+    }
+    return status;
+}
+
+/* Exact decoding of n raw 16-bit values (is_bf16: bfloat16, else binary16). */
+int oracle_bits_to_double(const uint16_t *bits, int is_bf16, int64_t n, double *out)
+{
+    if (!bits || !out || n < 0)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = is_bf16 ? bf16_bits_to_double(bits[i]) : half_bits_to_double(bits[i]);
+    return 0;
 }
 
 /* -------------------------------------------------------------- row softmax */

@@ -144,6 +144,58 @@ def test_splitkv_rejections():
     assert osc.attn_status_str(7) != "unknown status"
 
 
+def test_paged_decode_workspace_sizes():
+    """Bytes = segments * B*Hq*(D+2)*4; segments are whole 32-token tiles of
+    at most 2048 tokens; the automatic plan aims at about 1024 workgroups."""
+    f = osc.paged_decode_workspace
+    row = lambda B, Hq, D: B * Hq * (D + 2) * 4
+    assert f(8, 32, 8, 128, 16, 2048, 0) == 16 * row(8, 32, 128)   # 32K context: 16 x 2048
+    assert f(8, 32, 8, 128, 16, 64, 0) == 16 * row(8, 32, 128)     # 1K context: 16 x 64
+    assert f(1, 8, 1, 64, 1, 100, 0) == 4 * row(1, 8, 64)          # 4 tiles
+    assert f(1, 8, 1, 64, 1, 10, 0) == 0                           # one tile: no split
+    assert f(2, 16, 2, 128, 8, 200, 1) == 0                        # one segment requested
+    assert f(2, 16, 2, 128, 8, 300, 1) == 2 * row(2, 16, 128)      # 2400 tokens: raised to 2
+    assert f(1, 1, 1, 128, 16, 8192, 1) == 64 * row(1, 1, 128)     # 2048-token cap: 64 segments
+    assert f(5, 6, 3, 64, 32, 100, 7) == 7 * row(5, 6, 64)
+    for bad in [(8, 32, 8, 96, 16, 64, 0), (8, 33, 8, 128, 16, 64, 0), (8, 32, 8, 128, 12, 64, 0),
+                (8, 32, 8, 128, 16, 64, -1), (8, 32, 8, 128, 16, 64, 4097), (0, 32, 8, 128, 16, 64, 0),
+                (8, 64, 1, 128, 16, 64, 0), (8, 32, 8, 128, 1 << 17, 64, 0),
+                (8, 32, 8, 128, 16, 1 << 28, 0)]:
+        assert f(*bad) == -1, bad
+
+
+def call_decode(q=BASE, cache=BASE + 64 * MB, bt=BASE + 8192 * MB, lens=BASE + 8200 * MB,
+                o=BASE + 8300 * MB, lse=BASE + 8400 * MB, B=8, Hq=32, Hkv=8, D=128, T=16, P=512,
+                max_pages=64, dtype=0, splits=0, ws=BASE + 9000 * MB, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = max(osc.paged_decode_workspace(B, Hq, Hkv, D, T, max_pages, splits), 0)
+    return osc.load().paged_decode(q, cache, bt, lens, o, lse, B, Hq, Hkv, D, T, P, max_pages,
+                                   dtype, splits, ws, ws_bytes, None)
+
+
+def test_paged_decode_rejections():
+    need = osc.paged_decode_workspace(8, 32, 8, 128, 16, 64, 0)
+    assert need > 0
+    assert call_decode(q=None) == 1
+    assert call_decode(lens=None) == 1
+    assert call_decode(ws=None) == 1
+    assert call_decode(B=0) == 2
+    assert call_decode(Hq=30) == 2
+    assert call_decode(splits=-3) == 2
+    assert call_decode(D=80) == 3
+    assert call_decode(T=24) == 3
+    assert call_decode(Hq=64, Hkv=1) == 3            # group of 64 heads
+    assert call_decode(dtype=5) == 3
+    assert call_decode(q=BASE + 8) == 4
+    assert call_decode(bt=BASE + 8192 * MB + 2) == 4
+    assert call_decode(ws=BASE + 9000 * MB + 4) == 4
+    assert call_decode(ws_bytes=need - 4) == 7
+    assert call_decode(o=BASE + 64 * MB + 4096) == 6   # inside the cache
+    assert call_decode(lse=BASE + 8300 * MB + 16) == 6  # inside o
+    assert call_decode(ws=BASE + 8200 * MB - 64) == 6   # runs into lengths
+    assert call_decode(splits=1, ws=None, ws_bytes=0) != 1  # no workspace needed: not a NULL error
+
+
 def call_softmax(x=BASE, y=BASE + 64 * MB, M=4, N=100):
     return osc.load().row_softmax(x, y, M, N, None)
 

@@ -10,9 +10,11 @@ import os
 import subprocess
 
 import pytest
+import torch
 
 import oracle
 from tests import test_oracle as pins
+from tests import test_oracle_decode as dpins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -34,6 +36,24 @@ MUTANTS = {
                             "for (int64_t j = 1; j < N; ++j)\n        if (x[j] < m)"),
     "softmax_not_normalised": ("y[j] = y[j] / d;", "y[j] = y[j];"),
     "softmax_rows_shifted": ("softmax_row(jb->x + src * jb->N", "softmax_row(jb->x + (src / 2) * jb->N"),
+    # paged decode (every edit keeps the reads inside the buffers)
+    "dec_slot_off_by_one": ("dot += qr[d] * cache_at(jb, page, 0, t % jb->T, kvh, d);",
+                            "dot += qr[d] * cache_at(jb, page, 0, (t + 1) % jb->T, kvh, d);"),
+    "dec_head_interleaved": ("const int64_t kvh = h / (jb->Hq / jb->Hkv);",
+                             "const int64_t kvh = h % jb->Hkv;"),
+    "dec_v_read_from_k": ("o_row[d] += s[t] * cache_at(jb, page, 1,",
+                          "o_row[d] += s[t] * cache_at(jb, page, 0,"),
+    "dec_drops_last_token": ("const int64_t len = jb->lengths[b];",
+                             "const int64_t len = jb->lengths[b] > 1 ? jb->lengths[b] - 1 : jb->lengths[b];"),
+    "dec_first_page_only": ("const int64_t page = jb->block_table[b * jb->max_pages + t / jb->T];\n            double dot",
+                            "const int64_t page = jb->block_table[b * jb->max_pages];\n            double dot"),
+    "dec_scale_dropped": ("s[t] = dot / root_d;", "s[t] = dot;"),
+    "dec_query_of_head0": ("const double *qr = jb->q + flat * jb->D;",
+                           "const double *qr = jb->q + b * jb->Hq * jb->D;"),
+    "dec_bf16_read_as_fp16": ("jb->is_bf16 ? bf16_bits_to_double(jb->cache[idx]) : half_bits_to_double(jb->cache[idx])",
+                              "half_bits_to_double(jb->cache[idx])"),
+    "half_subnormal_scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    "half_exponent_bias": ("v = ldexp((double)(1024 + m), e - 25);", "v = ldexp((double)(1024 + m), e - 24);"),
 }
 
 PIN_CALLS = [
@@ -55,6 +75,16 @@ PIN_CALLS = [
     (pins.test_softmax_all_zero_is_uniform, {}),
     (pins.test_softmax_special_last_element_closed_form, {}),
     (pins.test_softmax_matches_library_routines, {}),
+    (dpins.test_fp16_bits_decode_exactly, {}),
+    (dpins.test_bf16_bits_decode_exactly, {}),
+    (dpins.test_equals_last_causal_row_of_attention, {"dtype": torch.float16, "T": 4, "Hkv": 2}),
+    (dpins.test_equals_last_causal_row_of_attention, {"dtype": torch.bfloat16, "T": 16, "Hkv": 4}),
+    (dpins.test_matches_torch_sdpa_float64, {}),
+    (dpins.test_single_token_returns_v0_and_its_logit, {}),
+    (dpins.test_identical_keys_give_the_mean_of_v, {}),
+    (dpins.test_physical_page_order_does_not_matter, {}),
+    (dpins.test_heads_of_a_group_share_their_kv_head, {}),
+    (dpins.test_invalid_requests_get_nan_and_others_are_unaffected, {}),
 ]
 
 

@@ -97,6 +97,49 @@ SPLITKV = {
     "S1": AttnWorkload("S1", 1, 2, 16384, 128, True, "f16", 1.0, 1.0, 52),
 }
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One paged grouped-query decode step ("CUDA KV Cache: paged storage and
+    long-context decode" (chengzipai.xyz), section 8: B=8, Hq=32, Hkv=8,
+    D=128, fp16, page size 16, context 1K to 32K, every request at the same
+    context length)."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    page_size: int
+    ctx: int
+    dtype: str
+    seed: int
+
+    @property
+    def max_pages(self) -> int:
+        return (self.ctx + self.page_size - 1) // self.page_size
+
+    @property
+    def num_pages(self) -> int:
+        """Cache pages: exactly the pages the requests use."""
+        return self.B * self.max_pages
+
+    @property
+    def bytes(self) -> float:
+        """Algorithmic bytes: K and V of every cached token read once, q read,
+        o (FP32) and lse written."""
+        kv = 2.0 * self.B * self.ctx * self.Hkv * self.D * 2
+        return kv + self.B * self.Hq * self.D * (2 + 4) + self.B * self.Hq * 4
+
+    def describe(self) -> str:
+        return "paged GQA decode %s B%d Hq%d Hkv%d D%d page%d ctx%d" % (
+            self.dtype, self.B, self.Hq, self.Hkv, self.D, self.page_size, self.ctx)
+
+
+DECODE = {
+    "D%d" % (ctx // 1024): DecodeWorkload("D%d" % (ctx // 1024), 8, 32, 8, 128, 16, ctx, "f16",
+                                          60 + i)
+    for i, ctx in enumerate((1024, 4096, 8192, 16384, 32768))
+}
+
 SOFTMAX = {
     "R1": SoftmaxWorkload("R1", 1025, 257, 80.0, 48),
     "R2": SoftmaxWorkload("R2", 8192, 32768, 80.0, 49),
@@ -134,6 +177,38 @@ def workload_inputs(w: AttnWorkload):
     if w.Hkv is not None:
         return gqa_inputs(w.B, w.H, w.Hkv, w.N, w.D, w.dtype, w.seed, w.sigma_qk, w.sigma_v)
     return attn_inputs(w.B, w.H, w.N, w.D, w.dtype, w.seed, w.sigma_qk, w.sigma_v)
+
+
+def decode_inputs(B: int, Hq: int, Hkv: int, D: int, page_size: int, num_pages: int,
+                  max_pages: int, lengths, dtype: str, seed: int, sigma_qk: float = 1.0,
+                  sigma_v: float = 1.0):
+    """q [B,Hq,D], cache [P,2,T,Hkv,D], block_table [B,max_pages] int32, lengths [B] int32.
+
+    Draw order: q, then K pages, then V pages (each float32 randn times its
+    sigma, rounded to the dtype); then one random permutation of the page
+    ids, dealt to the requests row by row, so every request's pages are
+    scattered over the cache (the page's Figure 1: logical pages map to
+    arbitrary physical pages).  Table entries past num_pages repeat page ids.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    td = TORCH_DTYPE[dtype]
+    q = (torch.randn((B, Hq, D), generator=g, dtype=torch.float32) * sigma_qk).to(td)
+    shape = (num_pages, page_size, Hkv, D)
+    k = (torch.randn(shape, generator=g, dtype=torch.float32) * sigma_qk).to(td)
+    v = (torch.randn(shape, generator=g, dtype=torch.float32) * sigma_v).to(td)
+    cache = torch.stack((k, v), dim=1).contiguous()
+    del k, v
+    perm = torch.randperm(num_pages, generator=g)
+    flat = perm.repeat((B * max_pages + num_pages - 1) // num_pages)[:B * max_pages]
+    block_table = flat.reshape(B, max_pages).to(torch.int32).contiguous()
+    lengths = torch.as_tensor(list(lengths), dtype=torch.int32).contiguous()
+    return q.contiguous(), cache, block_table, lengths
+
+
+def decode_workload_inputs(w: DecodeWorkload):
+    return decode_inputs(w.B, w.Hq, w.Hkv, w.D, w.page_size, w.num_pages, w.max_pages,
+                         [w.ctx] * w.B, w.dtype, w.seed)
 
 
 def softmax_inputs(M: int, N: int, seed: int, last: float | None = 80.0):
