@@ -19,6 +19,7 @@ One JSON line goes to stdout.  Besides the contract fields it carries:
   parity_sample max-abs error of the GPU output on those sampled rows;
   extra         the other configurations (C1, C2, C3, C5 attention; G1
                 grouped-query attention; S1 without and with the key split;
+                D1..D32 paged grouped-query decode at 1K..32K tokens;
                 R1, R2 row softmax), timed as the median of 7 group means of
                 back-to-back launches (FA page, section 8 method).
 Runs on one GPU only; --gpus above 1 exits with a message.
@@ -41,9 +42,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_C4_traffic.txt")
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(names=("attn_fwd.hip", "mfma_tile.hpp", "online_merge.hpp")) -> str:
+    """Short SHA-256 of kernel sources (by default the attention kernel's)."""
     h = hashlib.sha256()
-    for name in ("attn_fwd.hip", "online_merge.hpp"):
+    for name in names:
         with open(os.path.join(ROOT, "online_softmax_causal_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -137,6 +139,23 @@ def extra_configs(dev):
                               "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4),
                               "workspace_bytes": need if entry != "attn_fwd" else 0}
     del q, k, v, o, lse, ws
+    # Paged grouped-query decode (KV page, section 8 shapes), automatic split;
+    # attention kernel and merge inside the timed region.  HBM-bound: GB/s of
+    # algorithmic bytes (K and V of every cached token once, q, o, lse).
+    for name, w in workloads.DECODE.items():
+        q, cache, bt, ln = (t.to(dev) for t in workloads.decode_workload_inputs(w))
+        o = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+        need = osc.paged_decode_workspace(w.B, w.Hq, w.Hkv, w.D, w.page_size, w.max_pages, 0)
+        ws = torch.empty((max(need, 16) // 4,), dtype=torch.float32, device=dev)
+        fn = lambda: osc.paged_decode(q, cache, bt, ln, o, lse, w.B, w.Hq, w.Hkv, w.D,
+                                      w.page_size, w.num_pages, w.max_pages, w.dtype, 0, ws, need)
+        med, mn = time_groups(fn, stream)
+        gbs = w.bytes / (med * 1e-3) / 1e9
+        out[name] = {"workload": w.describe(), "entry": "paged_decode", "ms": round(med, 5),
+                     "ms_min": round(mn, 5), "gbs": round(gbs, 1),
+                     "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "workspace_bytes": need}
+        del q, cache, bt, ln, o, lse, ws
     for name in ("R1", "R2"):
         w = workloads.SOFTMAX[name]
         x = workloads.softmax_inputs(w.M, w.N, seed=w.seed, last=w.last).to(dev)
@@ -215,6 +234,25 @@ def profile_pass():
         dst.copy_(src)
     torch.cuda.synchronize()
     print("profile pass done", flush=True)
+
+
+def profile_decode(launches=30):
+    """Launch the 32K-context paged decode `launches` times (for rocprofv3)."""
+    import torch
+    import online_softmax_causal_amd as osc
+    import workloads
+    dev = torch.device("cuda:0")
+    w = workloads.DECODE["D32"]
+    q, cache, bt, ln = (t.to(dev) for t in workloads.decode_workload_inputs(w))
+    o = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    need = osc.paged_decode_workspace(w.B, w.Hq, w.Hkv, w.D, w.page_size, w.max_pages, 0)
+    ws = torch.empty((max(need, 16) // 4,), dtype=torch.float32, device=dev)
+    for _ in range(launches):
+        osc.paged_decode(q, cache, bt, ln, o, lse, w.B, w.Hq, w.Hkv, w.D, w.page_size,
+                         w.num_pages, w.max_pages, w.dtype, 0, ws, need)
+    torch.cuda.synchronize()
+    print("decode launches:", launches, w.describe(), "algorithmic bytes per launch", w.bytes)
 
 
 def _pmc_rows(path):
@@ -309,12 +347,15 @@ def summarize_trace(trace_dir, out_path, cmd, last):
                 (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     lines.append("")
     for name, d in durs.items():
-        if "attn_fwd_kernel" in name or "softmax" in name:
+        if any(k in name for k in ("attn_fwd_kernel", "softmax", "paged_decode", "splitkv_merge")):
             d.sort()
             tail = [x[1] for x in d[-last:]]
             lines.append("%s: mean of the last %d launches (the timed steps) %.2f us" % (
                 name[:110], len(tail), sum(tail) / len(tail) / 1e3))
-    lines.append("kernel_source_sha256_16: %s" % kernel_source_hash())
+    lines.append("sources_sha256_16: attn_fwd.hip+mfma_tile.hpp+online_merge.hpp %s, "
+                 "decode.hip %s, splitkv.hip %s" % (kernel_source_hash(),
+                                                   kernel_source_hash(("decode.hip",)),
+                                                   kernel_source_hash(("splitkv.hip",))))
     lines.append("")
     with open(out_path, "w") as f:
         f.write("\n".join(lines))
@@ -330,6 +371,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="run the fixed launch sequence the counter passes profile")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="only launch the 32K-context paged decode 30 times (for rocprofv3)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
     ap.add_argument("--trace-last", type=int, default=20)
@@ -346,6 +389,9 @@ def main():
         return
     if args.profile_pass:
         profile_pass()
+        return
+    if args.profile_decode:
+        profile_decode()
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

@@ -280,15 +280,17 @@ paged_decode_kernel(DecodeArgs a) {
 
 }  // namespace
 
-// Segments: the automatic plan aims at about 1024 workgroups (B * Hkv *
-// segments), so that with two resident workgroups per CU every CU gets
-// several; a caller's request > 0 is taken as is.  Segments are whole tiles
+// Segments: the automatic plan aims at about 512 workgroups (B * Hkv *
+// segments), one round of two resident workgroups per CU: more segments add
+// merge traffic and per-workgroup start-up for no extra bandwidth (measured
+// on the benchmark shapes, 1K to 32K tokens).  A caller's request > 0 is
+// taken as is.  Segments are whole tiles
 // and at most kDecMaxSegTokens tokens (the LDS page-id slots), so the count
 // is then raised to what the capacity needs.  Sized by the capacity
 // max_pages * T, since the lengths are device data the host does not read.
 DecodePlan paged_decode_plan(int64_t B, int64_t Hkv, int64_t cap, int requested) {
     const int64_t tiles = (cap + kDecTile - 1) / kDecTile;
-    int64_t want = requested > 0 ? requested : (1024 + B * Hkv - 1) / (B * Hkv);
+    int64_t want = requested > 0 ? requested : (512 + B * Hkv - 1) / (B * Hkv);
     if (want > tiles) want = tiles;
     if (want < 1) want = 1;
     int64_t seg_tiles = (tiles + want - 1) / want;

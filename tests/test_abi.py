@@ -146,11 +146,11 @@ def test_splitkv_rejections():
 
 def test_paged_decode_workspace_sizes():
     """Bytes = segments * B*Hq*(D+2)*4; segments are whole 32-token tiles of
-    at most 2048 tokens; the automatic plan aims at about 1024 workgroups."""
+    at most 2048 tokens; the automatic plan aims at about 512 workgroups."""
     f = osc.paged_decode_workspace
     row = lambda B, Hq, D: B * Hq * (D + 2) * 4
     assert f(8, 32, 8, 128, 16, 2048, 0) == 16 * row(8, 32, 128)   # 32K context: 16 x 2048
-    assert f(8, 32, 8, 128, 16, 64, 0) == 16 * row(8, 32, 128)     # 1K context: 16 x 64
+    assert f(8, 32, 8, 128, 16, 64, 0) == 8 * row(8, 32, 128)      # 1K context: 8 x 128
     assert f(1, 8, 1, 64, 1, 100, 0) == 4 * row(1, 8, 64)          # 4 tiles
     assert f(1, 8, 1, 64, 1, 10, 0) == 0                           # one tile: no split
     assert f(2, 16, 2, 128, 8, 200, 1) == 0                        # one segment requested
