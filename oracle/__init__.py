@@ -16,6 +16,8 @@ statement):
   mask j <= i) and section 3 (the naive three stages);
 * row softmax: the softmax kernel study (lpnh.cn/news/2830604), section 3.1
   (double-precision stable softmax as the CPU reference);
+* attention backward: the gradients of the attention definition (the FA
+  page, section 7, only says the LSE is kept for the backward pass);
 * paged decode: "CUDA KV Cache: paged storage and long-context decode"
   (chengzipai.xyz), sections 2 (page-table addressing), 3 (query-head groups
   share a K/V head) and 5 (attention of the new token over the cached ones).
@@ -59,6 +61,9 @@ def _bind(path: str):
     lib.oracle_attn_fwd.argtypes = [_PD, _PD, _PD, _PD, _PD, _I64, _I64, _I64, _I64,
                                     ctypes.c_int, ctypes.c_int]
     lib.oracle_attn_fwd.restype = ctypes.c_int
+    lib.oracle_attn_bwd.argtypes = [_PD, _PD, _PD, _PD, _I64, _I64, _I64, _I64, ctypes.c_int,
+                                    _PI64, _I64, _PD, _PD, _PD, ctypes.c_int]
+    lib.oracle_attn_bwd.restype = ctypes.c_int
     lib.oracle_paged_decode.argtypes = [_PD, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                         ctypes.c_void_p, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                         _PI64, _I64, _PD, _PD, ctypes.c_int]
@@ -160,6 +165,33 @@ def attn_rows(q, k, v, causal: bool, rows, nthreads: int | None = None):
     if rc != 0:
         raise RuntimeError("oracle_attn_rows failed (%d)" % rc)
     return o, lse
+
+
+def attn_bwd(q, k, v, dout, causal: bool, heads=None, nthreads: int | None = None):
+    """Gradients dQ, dK, dV of sum(O * dout) for O = attention(q, k, v).
+
+    Inputs [B,H,N,D] (any float type).  heads: flat head ids b*H + h to
+    compute (all if None).  Returns three float64 arrays [len(heads), N, D]
+    (reshaped to [B,H,N,D] when heads is None).
+    """
+    q, k, v, dout = to_f64(q), to_f64(k), to_f64(v), to_f64(dout)
+    B, H, N, D = q.shape
+    for x in (k, v, dout):
+        assert x.shape == q.shape
+    all_heads = heads is None
+    heads = np.arange(B * H) if all_heads else heads
+    heads = np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+    dq = np.empty((heads.size, N, D), np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    rc = _load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, D,
+                                 int(bool(causal)), heads.ctypes.data_as(_PI64), heads.size,
+                                 _ptr(dq), _ptr(dk), _ptr(dv), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle_attn_bwd failed (%d)" % rc)
+    if all_heads:
+        return dq.reshape(B, H, N, D), dk.reshape(B, H, N, D), dv.reshape(B, H, N, D)
+    return dq, dk, dv
 
 
 def kv_head(h: int, H: int, Hkv: int) -> int:

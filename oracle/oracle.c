@@ -21,6 +21,19 @@
  *   sum_j exp(s_ij) over the same keys (the page's section 7 only says the
  *   LSE is saved for the backward pass; this is the plain reading).
  *
+ *   Attention backward: the pages only say that training keeps (or
+ *   recomputes) the log-sum-exp for the backward pass (FA page, section 7)
+ *   and that their kernels are forward-only (section 9).  The gradients are
+ *   therefore the calculus of the definition above: for the loss L with
+ *   dL/dO = dO and P the softmax weights of row i,
+ *     dV_j = sum_i P_ij dO_i,       dP_ij = dO_i . v_j,
+ *     D_i  = sum_j P_ij dP_ij,      dS_ij = P_ij (dP_ij - D_i),
+ *     dQ_i = sum_j dS_ij k_j / sqrt(D),   dK_j = sum_i dS_ij q_i / sqrt(D),
+ *   over the visible pairs (j <= i when causal).  Pass 1 walks the rows
+ *   (P, dP, D_i, dS and dQ_i; m_i, l_i, D_i kept); pass 2 walks the keys,
+ *   recomputing P_ij and dS_ij from the kept row statistics, so every sum
+ *   runs in a fixed order whatever the thread count.
+ *
  *   Paged decode, from "CUDA KV Cache: paged storage and long-context
  *   decode" (chengzipai.xyz), sections 2, 3 and 5: one query per (request b,
  *   query head h) attends over the request's len_b cached tokens.  Token t of
@@ -200,6 +213,168 @@ int64_t oracle_attn_scores(const double *q, const double *k, int64_t N, int64_t 
     if (!q || !k || !s || N < 1 || D < 1 || i < 0 || i >= N)
         return -1;
     return scores_row(q, k, N, D, causal, i, s);
+}
+
+/* ------------------------------------------------------- attention backward */
+
+typedef struct {
+    const double *q, *k, *v, *dout;   /* one head: [N, D] each */
+    double *dq, *dk, *dv;             /* one head: [N, D] each */
+    double *m, *l, *dd;               /* row statistics [N] */
+    int64_t N, D;
+    int causal;
+    int64_t begin, end;               /* rows (pass 1) or keys (pass 2) */
+    int pass;
+    int status;
+} bwd_job;
+
+static void *bwd_worker(void *arg)
+{
+    bwd_job *jb = (bwd_job *)arg;
+    const int64_t N = jb->N, D = jb->D;
+    const double root_d = sqrt((double)D);
+    if (jb->pass == 1) {
+        double *s = (double *)malloc((size_t)N * sizeof(double));
+        double *dp = (double *)malloc((size_t)N * sizeof(double));
+        if (!s || !dp) {
+            free(s);
+            free(dp);
+            jb->status = -2;
+            return NULL;
+        }
+        for (int64_t i = jb->begin; i < jb->end; ++i) {
+            const int64_t nkeys = scores_row(jb->q, jb->k, N, D, jb->causal, i, s);
+            double m = s[0];
+            for (int64_t j = 1; j < nkeys; ++j)
+                if (s[j] > m)
+                    m = s[j];
+            double l = 0.0;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                s[j] = exp(s[j] - m);
+                l += s[j];
+            }
+            for (int64_t j = 0; j < nkeys; ++j)
+                s[j] = s[j] / l;                       /* P_ij */
+            const double *doi = jb->dout + i * D;
+            double dd = 0.0;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                const double *vj = jb->v + j * D;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += doi[d] * vj[d];
+                dp[j] = dot;                           /* dP_ij */
+                dd += s[j] * dot;
+            }
+            double *dqi = jb->dq + i * D;
+            for (int64_t d = 0; d < D; ++d)
+                dqi[d] = 0.0;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                const double ds = s[j] * (dp[j] - dd);  /* dS_ij */
+                const double *kj = jb->k + j * D;
+                for (int64_t d = 0; d < D; ++d)
+                    dqi[d] += ds * kj[d];
+            }
+            for (int64_t d = 0; d < D; ++d)
+                dqi[d] /= root_d;
+            jb->m[i] = m;
+            jb->l[i] = l;
+            jb->dd[i] = dd;
+        }
+        free(s);
+        free(dp);
+    } else {
+        for (int64_t j = jb->begin; j < jb->end; ++j) {
+            const double *kj = jb->k + j * D, *vj = jb->v + j * D;
+            double *dkj = jb->dk + j * D, *dvj = jb->dv + j * D;
+            for (int64_t d = 0; d < D; ++d) {
+                dkj[d] = 0.0;
+                dvj[d] = 0.0;
+            }
+            for (int64_t i = jb->causal ? j : 0; i < N; ++i) {
+                const double *qi = jb->q + i * D, *doi = jb->dout + i * D;
+                double sdot = 0.0, pdot = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    sdot += qi[d] * kj[d];
+                    pdot += doi[d] * vj[d];
+                }
+                const double p = exp(sdot / root_d - jb->m[i]) / jb->l[i];
+                const double ds = p * (pdot - jb->dd[i]);
+                for (int64_t d = 0; d < D; ++d) {
+                    dvj[d] += p * doi[d];
+                    dkj[d] += ds * qi[d];
+                }
+            }
+            for (int64_t d = 0; d < D; ++d)
+                dkj[d] /= root_d;
+        }
+    }
+    jb->status = 0;
+    return NULL;
+}
+
+static int run_bwd_pass(bwd_job proto, int pass, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if ((int64_t)nthreads > proto.N)
+        nthreads = (int)proto.N;
+    bwd_job jobs[256];
+    pthread_t tid[256];
+    int started[256] = {0};
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = proto;
+        jobs[t].pass = pass;
+        jobs[t].begin = proto.N * t / nthreads;
+        jobs[t].end = proto.N * (t + 1) / nthreads;
+        jobs[t].status = -2;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        started[t] = pthread_create(&tid[t], NULL, bwd_worker, &jobs[t]) == 0;
+    bwd_worker(&jobs[0]);
+    int status = jobs[0].status;
+    for (int t = 1; t < nthreads; ++t) {
+        if (started[t])
+            pthread_join(tid[t], NULL);
+        else
+            bwd_worker(&jobs[t]);
+        if (jobs[t].status != 0)
+            status = jobs[t].status;
+    }
+    return status;
+}
+
+/* Gradients of the selected heads heads[h] = b*H + h' of [B,H,N,D] inputs;
+ * dq, dk, dv are [nheads, N, D]. */
+int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
+                    int64_t B, int64_t H, int64_t N, int64_t D, int causal, const int64_t *heads,
+                    int64_t nheads, double *dq, double *dk, double *dv, int nthreads)
+{
+    if (!q || !k || !v || !dout || !heads || !dq || !dk || !dv || B < 1 || H < 1 || N < 1 ||
+        D < 1 || nheads < 0)
+        return -1;
+    for (int64_t h = 0; h < nheads; ++h)
+        if (heads[h] < 0 || heads[h] >= B * H)
+            return -1;
+    double *m = (double *)malloc((size_t)N * sizeof(double));
+    double *l = (double *)malloc((size_t)N * sizeof(double));
+    double *dd = (double *)malloc((size_t)N * sizeof(double));
+    int status = 0;
+    if (!m || !l || !dd)
+        status = -2;
+    for (int64_t h = 0; status == 0 && h < nheads; ++h) {
+        const int64_t off = heads[h] * N * D, out = h * N * D;
+        bwd_job proto = {q + off, k + off, v + off, dout + off, dq + out, dk + out, dv + out,
+                         m, l, dd, N, D, causal, 0, 0, 0, 0};
+        status = run_bwd_pass(proto, 1, nthreads);
+        if (status == 0)
+            status = run_bwd_pass(proto, 2, nthreads);
+    }
+    free(m);
+    free(l);
+    free(dd);
+    return status;
 }
 
 /* ------------------------------------------------------------- paged decode */

@@ -14,6 +14,7 @@ import torch
 
 import oracle
 from tests import test_oracle as pins
+from tests import test_oracle_bwd as bpins
 from tests import test_oracle_decode as dpins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
@@ -53,6 +54,18 @@ MUTANTS = {
     "dec_bf16_read_as_fp16": ("jb->is_bf16 ? bf16_bits_to_double(jb->cache[idx]) : half_bits_to_double(jb->cache[idx])",
                               "half_bits_to_double(jb->cache[idx])"),
     "half_subnormal_scale": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    # attention backward
+    "bwd_no_d_term": ("const double ds = s[j] * (dp[j] - dd);  /* dS_ij */",
+                      "const double ds = s[j] * dp[j];  /* dS_ij */"),
+    "bwd_dq_unscaled": ("dqi[d] /= root_d;", "dqi[d] /= 1.0;"),
+    "bwd_dk_unscaled": ("dkj[d] /= root_d;", "dkj[d] /= 1.0;"),
+    "bwd_dv_uses_ds": ("dvj[d] += p * doi[d];", "dvj[d] += ds * doi[d];"),
+    "bwd_dp_uses_k": ("pdot += doi[d] * vj[d];", "pdot += doi[d] * kj[d];"),
+    "bwd_causal_skips_diagonal": ("for (int64_t i = jb->causal ? j : 0; i < N; ++i) {",
+                                  "for (int64_t i = jb->causal ? j + 1 : 0; i < N; ++i) {"),
+    "bwd_dk_uses_k": ("dkj[d] += ds * qi[d];", "dkj[d] += ds * kj[d];"),
+    "bwd_p_not_normalised": ("const double p = exp(sdot / root_d - jb->m[i]) / jb->l[i];",
+                             "const double p = exp(sdot / root_d - jb->m[i]);"),
     "half_exponent_bias": ("v = ldexp((double)(1024 + m), e - 25);", "v = ldexp((double)(1024 + m), e - 24);"),
 }
 
@@ -75,6 +88,11 @@ PIN_CALLS = [
     (pins.test_softmax_all_zero_is_uniform, {}),
     (pins.test_softmax_special_last_element_closed_form, {}),
     (pins.test_softmax_matches_library_routines, {}),
+    (bpins.test_matches_torch_autograd_float64, {"shape": (1, 2, 9, 8), "causal": True}),
+    (bpins.test_central_differences_of_the_forward_oracle, {"causal": True}),
+    (bpins.test_key_gradients_sum_to_zero_and_dv_to_the_dout_sum, {"causal": True}),
+    (bpins.test_single_key_and_identical_keys, {}),
+    (bpins.test_causal_dependency_structure_is_exact, {}),
     (dpins.test_fp16_bits_decode_exactly, {}),
     (dpins.test_bf16_bits_decode_exactly, {}),
     (dpins.test_equals_last_causal_row_of_attention, {"dtype": torch.float16, "T": 4, "Hkv": 2}),
