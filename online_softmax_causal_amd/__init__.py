@@ -17,6 +17,9 @@ The entry points mirror the C ABI in ``include/osc_attn.h``:
                  num_pages, max_pages, dtype, num_splits, workspace, workspace_bytes,
                  stream=None)
     paged_decode_workspace(B, Hq, Hkv, D, page_size, max_pages, num_splits=0)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, dtype, workspace,
+             workspace_bytes, stream=None)
+    attn_bwd_workspace(B, H, N)
     attn_status_str(status)
 
 Pointer arguments accept device tensors (``torch.Tensor``, only its address is
@@ -46,7 +49,8 @@ STATUS = {
     7: "ATTN_ERR_WORKSPACE",
 }
 EXPORTS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace",
-           "paged_decode", "paged_decode_workspace", "row_softmax", "attn_status_str")
+           "paged_decode", "paged_decode_workspace", "attn_bwd", "attn_bwd_workspace",
+           "row_softmax", "attn_status_str")
 
 _lib = None
 
@@ -83,6 +87,11 @@ def load():
     lib.paged_decode.restype = ctypes.c_int
     lib.paged_decode_workspace.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     lib.paged_decode_workspace.restype = i64
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                             ctypes.c_int, vp, i64, vp]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace.argtypes = [i64, i64, i64]
+    lib.attn_bwd_workspace.restype = i64
     lib.row_softmax.argtypes = [vp, vp, i64, i64, vp]
     lib.row_softmax.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
@@ -175,6 +184,21 @@ def paged_decode(q, cache, block_table, lengths, o, lse, B, Hq, Hkv, D, page_siz
                              _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != 0:
         raise AttnError(st, "paged_decode")
+
+
+def attn_bwd_workspace(B, H, N) -> int:
+    """Workspace bytes attn_bwd needs (8 * B*H*N); -1 if invalid."""
+    return int(load().attn_bwd_workspace(int(B), int(H), int(N)))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, dtype, workspace,
+             workspace_bytes, stream=None) -> None:
+    """Enqueue attention backward (dq, dk, dv FP32) from the forward's o and lse."""
+    st = load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                         _ptr(dk), _ptr(dv), int(B), int(H), int(N), int(D), int(bool(causal)),
+                         _dtype(dtype), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
 
 
 def row_softmax(x, y, M, N, stream=None) -> None:

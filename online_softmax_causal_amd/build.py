@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libosc_attn.so")
-SOURCES = ["attn_fwd.hip", "decode.hip", "splitkv.hip", "row_softmax.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "bwd.hip", "decode.hip", "splitkv.hip", "row_softmax.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -37,8 +37,8 @@ def _compile(src: str) -> str:
 
 
 def check_m0(src: str) -> None:
-    """The attention and decode kernels write M0 in inline assembly (the LDS
-    address of global_load_lds_dwordx4).  That is only safe while no compiler-generated
+    """The attention, backward and decode kernels write M0 in inline assembly
+    (the LDS address of global_load_lds_dword[x4]).  That is only safe while no compiler-generated
     instruction uses M0, so check the generated gfx950 assembly: every M0
     reference must be one of those writes, directly followed by the copy."""
     asm = os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
@@ -51,7 +51,7 @@ def check_m0(src: str) -> None:
     for i, ln in enumerate(lines):
         if "m0" in ln.replace(",", " ").split():
             ok = ln.startswith("s_mov_b32 m0,") and i + 1 < len(lines) and \
-                lines[i + 1].startswith("global_load_lds_dwordx4")
+                lines[i + 1].startswith("global_load_lds_dword")
             if not ok:
                 raise RuntimeError("unexpected use of M0 in %s: %r" % (src, ln))
 
@@ -60,7 +60,7 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
-        m0 = [ex.submit(check_m0, src) for src in ("attn_fwd.hip", "decode.hip")]
+        m0 = [ex.submit(check_m0, src) for src in ("attn_fwd.hip", "decode.hip", "bwd.hip")]
         objs = list(ex.map(_compile, SOURCES))
         for f in m0:
             f.result()

@@ -1,0 +1,483 @@
+// Attention backward on gfx950: dQ, dK, dV of O = softmax(Q K^T / sqrt(D) + M) V
+// for a given dO, from the forward pass's O and log-sum-exp.
+//
+// The pages keep the log-sum-exp of each row for the backward pass ("CUDA
+// FlashAttention: from online softmax to long-sequence IO limits"
+// (chengzipai.xyz), section 7) and give no backward algorithm of their own.
+// With it the softmax weights are recomputed tile by tile, P_ij =
+// exp(s_ij / sqrt(D) - lse_i), so nothing N x N is ever stored, and the
+// gradients are those of the definition:
+//     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_d dO_id O_id,
+//     dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D)
+// (D_i = sum_j P_ij dP_ij because O_i = sum_j P_ij v_j).
+//
+// Three kernels, all on one stream:
+//   attn_bwd_pre_kernel   D_i and the base-2 log-sum-exp lse_i * log2(e) of
+//                         every row, into the caller's workspace (HBM-bound);
+//   attn_bwd_dkdv_kernel  key-major: a workgroup keeps 128 keys (32 per wave)
+//                         of K and V in registers and streams 64-row tiles of
+//                         Q and dO (with D and lse of those rows) through LDS;
+//                         dV^T += dO^T P and dK^T += Q^T dS on the MFMA;
+//   attn_bwd_dq_kernel    query-major, like the forward kernel: a workgroup
+//                         keeps 128 query rows of Q and dO in registers and
+//                         streams 64-key tiles of K and V; dQ^T += K^T dS^T.
+// Splitting dQ from dK/dV recomputes S and dP once more but needs no atomic
+// accumulation, so the result is deterministic.  P and dS are rounded RNE to
+// the input dtype as MFMA operands; every accumulation is FP32.
+//
+// Operand layouts are those of the forward kernel (32x32x16 MFMA, chunk
+// swizzle, direct global->LDS copies, transpose reads for X^T operands):
+//   dK/dV kernel: S = Q K^T with A = Q rows from LDS and B = K^T in
+//   registers, so a lane holds one key (column) and 16 query rows; those
+//   accumulators, packed, are the B operand of dV^T = dO^T P whose A operand
+//   dO^T is read transposed from the dO tile in the same query order.
+//   dQ kernel: S^T = K Q^T exactly as the forward's; dS^T packed is the B
+//   operand of dQ^T = K^T dS^T with K^T read transposed from the K tile.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+#include "mfma_tile.hpp"
+#include "online_merge.hpp"
+
+namespace osc {
+namespace {
+
+constexpr int kBwdWaves = 4;            // waves per workgroup (one per SIMD)
+constexpr int kBwdRows = 32 * kBwdWaves; // resident rows (keys or queries) per workgroup
+constexpr int kBwdTile = 64;            // streamed rows per tile
+constexpr int kBwdStages = 3;           // LDS stages; tile t+2 is copied during tile t
+
+struct BwdArgs {
+    const u16* q;       // [B, H, N, D]
+    const u16* k;
+    const u16* v;
+    const float* o;     // [B, H, N, D] forward output
+    const float* lse;   // [B, H, N] forward log-sum-exp (natural log)
+    const u16* dout;    // [B, H, N, D]
+    float* dq;          // [B, H, N, D]
+    float* dk;
+    float* dv;
+    float* dd;          // workspace [B, H, N]: D_i
+    float* lse2;        // workspace [B, H, N]: lse_i * log2(e)
+    int BH;
+    int N;
+    float scale_log2;   // log2(e) / sqrt(D)
+    float scale;        // 1 / sqrt(D)
+};
+
+// Workgroup index -> (tile of resident rows, head), longest causal work first
+// for the key-major kernel (tile 0 sees every query) and for the query-major
+// kernel (the last tile sees every key); heads are spread over the XCDs as in
+// the forward kernel.
+__device__ __forceinline__ void bwd_work(int bid, int BH, int ntiles, bool reverse, int* tile,
+                                         int* bh) {
+    const int tt = bid / BH;
+    *tile = reverse ? ntiles - 1 - tt : tt;
+    const int j = bid % BH;
+    *bh = (BH & 7) ? j : (j & 7) * (BH >> 3) + (j >> 3);
+}
+
+// Copy rows [row0, row0 + 64) of a [N, D] 16-bit matrix into an LDS tile
+// (chunk-swizzled rows); the four waves share the 1 KiB blocks.  Rows past N
+// repeat row N - 1 (finite data; the kernels mask them).
+template <int D>
+__device__ __forceinline__ void copy_tile(const u16* src, u16* dst, int row0, int N, int w,
+                                          int lane) {
+    constexpr int CPR = D / 8, RPB = 1024 / (2 * D);
+    constexpr int BPW = kBwdTile / RPB / kBwdWaves;
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        const int blk = w * BPW + j;
+        const int r = blk * RPB + lane / CPR;
+        const int c = (lane % CPR) ^ chunk_swizzle<D>(r);
+        const int row = min(row0 + r, N - 1);
+        copy_to_lds16(src, (unsigned)((row * D + c * 8) * 2), dst + blk * 512);
+    }
+}
+
+template <int D>
+constexpr int copies_per_matrix() {
+    return kBwdTile / (1024 / (2 * D)) / kBwdWaves;
+}
+
+// One 16-bit value (low bits of b) as FP32, exactly.
+template <bool BF16>
+__device__ __forceinline__ float bits16_to_float(unsigned b) {
+    if constexpr (BF16)
+        return __builtin_bit_cast(float, b << 16);
+    else
+        return (float)__builtin_bit_cast(_Float16, (unsigned short)b);
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_d dO_id O_id and lse2_i = lse_i log2(e).  D / 8 lanes per row,
+// each lane 8 values (a 16-byte dO load and two 16-byte O loads).
+template <bool BF16, int D>
+__global__ void __launch_bounds__(256)
+attn_bwd_pre_kernel(BwdArgs a) {
+    constexpr int LPR = D / 8;
+    const int64_t rows = (int64_t)a.BH * a.N;
+    const int64_t r = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+    const int c = (threadIdx.x % LPR) * 8;
+    float acc = 0.0f;
+    if (r < rows) {
+        const u32x4 d16 = *reinterpret_cast<const u32x4*>(a.dout + r * D + c);
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(a.o + r * D + c);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(a.o + r * D + c + 4);
+        const float ov[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const unsigned w = d16[i];
+            acc = fmaf(bits16_to_float<BF16>(w & 0xffffu), ov[2 * i], acc);
+            acc = fmaf(bits16_to_float<BF16>(w >> 16), ov[2 * i + 1], acc);
+        }
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+    if (r < rows && threadIdx.x % LPR == 0) {
+        a.dd[r] = acc;
+        a.lse2[r] = a.lse[r] * kLog2e;
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <bool BF16, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+attn_bwd_dkdv_kernel(BwdArgs a) {
+    using M = Mma<BF16>;
+    constexpr int KS = D / 16, MT = D / 32;
+    constexpr int TILE = kBwdTile * D;
+    constexpr int STAGE = 2 * TILE + 2 * kBwdTile * 2;  // Q, dO (16-bit), lse2, D (FP32)
+    constexpr int LPM = copies_per_matrix<D>();
+    __shared__ __attribute__((aligned(1024))) u16 lds[kBwdStages * STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 31, g = lane >> 5;
+    const int N = a.N;
+    const int nkt = (N + kBwdRows - 1) / kBwdRows;
+    int kt, bh;
+    bwd_work(blockIdx.x, a.BH, nkt, false, &kt, &bh);
+    const int64_t head = (int64_t)bh * N;
+    const int kw = kt * kBwdRows + 32 * w;  // first key of this wave
+    const int key = kw + col;
+
+    // K^T and V^T fragments (B operands): lane (col, g) holds key `key`,
+    // d = 16 ks + 8 g .. + 7.
+    u32x4 kf[KS], vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int64_t off = (head + key) * D + ks * 16 + 8 * g;
+        kf[ks] = key < N ? *reinterpret_cast<const u32x4*>(a.k + off) : u32x4{0u, 0u, 0u, 0u};
+        vf[ks] = key < N ? *reinterpret_cast<const u32x4*>(a.v + off) : u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x16 dk_acc[MT], dv_acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        dk_acc[mt] = f32x16{};
+        dv_acc[mt] = f32x16{};
+    }
+    int rfo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) rfo[ks] = row_frag_offset<D>(col, ks, lane);
+    int tfo[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) tfo[mt][r] = tr_frag_offset<D>(lane, mt, r);
+
+    // Query tiles: with causal masking only rows at or after the workgroup's
+    // first key contribute.
+    const int nqt = (N + kBwdTile - 1) / kBwdTile;
+    const int qt0 = CAUSAL ? (kt * kBwdRows) / kBwdTile : 0;
+    auto stage = [&](int it) { return lds + (it % kBwdStages) * STAGE; };
+    // Waves 0 and 1 also copy the tile's lse2 and D rows (one 4-byte copy each).
+    auto issue = [&](int it) {
+        if (it >= nqt) return;
+        u16* st = stage(it);
+        const int r0 = it * kBwdTile;
+        copy_tile<D>(a.q + head * D, st, r0, N, w, lane);
+        copy_tile<D>(a.dout + head * D, st + TILE, r0, N, w, lane);
+        if (w < 2) {
+            const int row = min(r0 + lane, N - 1);
+            const float* src = w == 0 ? a.lse2 + head : a.dd + head;
+            copy_to_lds4(src, (unsigned)(row * 4), st + 2 * TILE + w * 2 * kBwdTile);
+        }
+    };
+    auto wait_next = [&](int it) {  // tile it+1 landed for this wave
+        if (it + 2 < nqt) {
+            if (w < 2)
+                wait_vmcnt<2 * LPM + 1>();
+            else
+                wait_vmcnt<2 * LPM>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+    };
+
+    issue(qt0);
+    issue(qt0 + 1);
+    if (qt0 + 1 < nqt) {
+        if (w < 2)
+            wait_vmcnt<2 * LPM + 1>();
+        else
+            wait_vmcnt<2 * LPM>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    __syncthreads();
+
+    for (int it = qt0; it < nqt; ++it) {
+        issue(it + 2);
+        const u16* qt = stage(it);
+        const u16* dot = qt + TILE;
+        const float* l2t = reinterpret_cast<const float*>(qt + 2 * TILE);
+        const float* ddt = l2t + kBwdTile;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int qb = it * kBwdTile + 32 * b;  // first query row of the block
+            if (qb >= N || (CAUSAL && qb + 31 < kw)) continue;
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s = M::run(*reinterpret_cast<const u32x4*>(qt + 32 * b * D + rfo[ks]), kf[ks], s);
+                dp = M::run(*reinterpret_cast<const u32x4*>(dot + 32 * b * D + rfo[ks]), vf[ks], dp);
+            }
+            // Lane (col, g) holds query rows qb + 8(e/4) + 4g + e%4 of key `key`.
+            const bool edge = (CAUSAL && qb < kw + 31) || qb + 32 > N;
+            float p[16], ds[16];
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const f32x4 l2 = *reinterpret_cast<const f32x4*>(l2t + 32 * b + 8 * j4 + 4 * g);
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(ddt + 32 * b + 8 * j4 + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * j4 + i;
+                    float pe = fast_exp2(fmaf(s[e], a.scale_log2, -l2[i]));
+                    if (edge) {
+                        const int qrow = qb + 8 * j4 + 4 * g + i;
+                        if ((CAUSAL && key > qrow) || qrow >= N) pe = 0.0f;
+                    }
+                    p[e] = pe;
+                    ds[e] = pe * (dp[e] - dd[i]);
+                }
+            }
+            u32x4 pf[2], dsf[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                pf[u] = u32x4{M::pack(p[8 * u], p[8 * u + 1]), M::pack(p[8 * u + 2], p[8 * u + 3]),
+                              M::pack(p[8 * u + 4], p[8 * u + 5]), M::pack(p[8 * u + 6], p[8 * u + 7])};
+                dsf[u] = u32x4{M::pack(ds[8 * u], ds[8 * u + 1]), M::pack(ds[8 * u + 2], ds[8 * u + 3]),
+                               M::pack(ds[8 * u + 4], ds[8 * u + 5]), M::pack(ds[8 * u + 6], ds[8 * u + 7])};
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS: A operands read transposed,
+            // 16 query rows per step, in the accumulator's row order.
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const u16* dog = dot + (32 * b + 16 * u) * D;
+                const u16* qg = qt + (32 * b + 16 * u) * D;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    dv_acc[mt] = M::run(tr16_b64x2(dog + tfo[mt][0], dog + tfo[mt][1]), pf[u], dv_acc[mt]);
+                    dk_acc[mt] = M::run(tr16_b64x2(qg + tfo[mt][0], qg + tfo[mt][1]), dsf[u], dk_acc[mt]);
+                }
+            }
+        }
+        wait_next(it);
+    }
+
+    // Lane (col, g) holds d = 32 mt + 8 (i / 4) + 4 g + i % 4 of key `key`.
+    if (key >= N) return;
+    float* dkr = a.dk + (head + key) * D;
+    float* dvr = a.dv + (head + key) * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int d = mt * 32 + 8 * i4 + 4 * g;
+            *reinterpret_cast<f32x4*>(dkr + d) =
+                f32x4{dk_acc[mt][4 * i4], dk_acc[mt][4 * i4 + 1], dk_acc[mt][4 * i4 + 2],
+                      dk_acc[mt][4 * i4 + 3]} * a.scale;
+            *reinterpret_cast<f32x4*>(dvr + d) =
+                f32x4{dv_acc[mt][4 * i4], dv_acc[mt][4 * i4 + 1], dv_acc[mt][4 * i4 + 2],
+                      dv_acc[mt][4 * i4 + 3]};
+        }
+}
+
+// ---------------------------------------------------------------------------
+template <bool BF16, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+attn_bwd_dq_kernel(BwdArgs a) {
+    using M = Mma<BF16>;
+    constexpr int KS = D / 16, MT = D / 32;
+    constexpr int TILE = kBwdTile * D;
+    constexpr int STAGE = 2 * TILE;  // K, V
+    constexpr int LPM = copies_per_matrix<D>();
+    __shared__ __attribute__((aligned(1024))) u16 lds[kBwdStages * STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 31, g = lane >> 5;
+    const int N = a.N;
+    const int nq = (N + kBwdRows - 1) / kBwdRows;
+    int t, bh;
+    bwd_work(blockIdx.x, a.BH, nq, CAUSAL, &t, &bh);
+    const int64_t head = (int64_t)bh * N;
+    const int row0 = t * kBwdRows + 32 * w;  // first query row of this wave
+    const int row = row0 + col;
+
+    u32x4 qf[KS], dof[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int64_t off = (head + row) * D + ks * 16 + 8 * g;
+        qf[ks] = row < N ? *reinterpret_cast<const u32x4*>(a.q + off) : u32x4{0u, 0u, 0u, 0u};
+        dof[ks] = row < N ? *reinterpret_cast<const u32x4*>(a.dout + off) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const float l2 = row < N ? a.lse2[head + row] : 0.0f;
+    const float dd = row < N ? a.dd[head + row] : 0.0f;
+    f32x16 dq_acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) dq_acc[mt] = f32x16{};
+    int rfo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) rfo[ks] = row_frag_offset<D>(col, ks, lane);
+    int tfo[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) tfo[mt][r] = tr_frag_offset<D>(lane, mt, r);
+
+    const int kv_end = CAUSAL ? min(t * kBwdRows + kBwdRows, N) : N;
+    const int ntiles = (kv_end + kBwdTile - 1) / kBwdTile;
+    // This wave's last key tile (none if its rows are past N).
+    const int last = row0 >= N ? -1 : min(ntiles - 1, CAUSAL ? (row0 + 31) / kBwdTile : ntiles - 1);
+    auto stage = [&](int it) { return lds + (it % kBwdStages) * STAGE; };
+    auto issue = [&](int it) {
+        if (it >= ntiles) return;
+        u16* st = stage(it);
+        copy_tile<D>(a.k + head * D, st, it * kBwdTile, N, w, lane);
+        copy_tile<D>(a.v + head * D, st + TILE, it * kBwdTile, N, w, lane);
+    };
+
+    issue(0);
+    issue(1);
+    if (1 < ntiles)
+        wait_vmcnt<2 * LPM>();
+    else
+        wait_vmcnt<0>();
+    __syncthreads();
+
+    for (int it = 0; it < ntiles; ++it) {
+        issue(it + 2);
+        if (it <= last) {
+            const u16* kt = stage(it);
+            const u16* vt = kt + TILE;
+            // S^T and dP^T for keys 32 kb + (accumulator rows): lane (col, g)
+            // holds keys 32 kb + 8 (e / 4) + 4 g + e % 4 of query `row`.
+            f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    s[kb] = M::run(*reinterpret_cast<const u32x4*>(kt + 32 * kb * D + rfo[ks]), qf[ks], s[kb]);
+                    dp[kb] = M::run(*reinterpret_cast<const u32x4*>(vt + 32 * kb * D + rfo[ks]), dof[ks], dp[kb]);
+                }
+            const int key0 = it * kBwdTile;
+            const bool edge = (CAUSAL && key0 + kBwdTile - 1 > row0) || key0 + kBwdTile > N;
+            u32x4 dsf[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int kb = u >> 1, h = (u & 1) * 8;
+                float ds[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int e = h + jj;
+                    float pe = fast_exp2(fmaf(s[kb][e], a.scale_log2, -l2));
+                    if (edge) {
+                        const int kidx = key0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+                        if ((CAUSAL && kidx > row) || kidx >= N) pe = 0.0f;
+                    }
+                    ds[jj] = pe * (dp[kb][e] - dd);
+                }
+                dsf[u] = u32x4{M::pack(ds[0], ds[1]), M::pack(ds[2], ds[3]), M::pack(ds[4], ds[5]),
+                               M::pack(ds[6], ds[7])};
+            }
+            // dQ^T += K^T dS^T: K^T read transposed, 16 keys per step.
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const u16* kg = kt + 16 * u * D;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    dq_acc[mt] = M::run(tr16_b64x2(kg + tfo[mt][0], kg + tfo[mt][1]), dsf[u], dq_acc[mt]);
+            }
+        }
+        if (it + 2 < ntiles)
+            wait_vmcnt<2 * LPM>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+    }
+
+    if (row >= N) return;
+    float* dqr = a.dq + (head + row) * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+            *reinterpret_cast<f32x4*>(dqr + mt * 32 + 8 * i4 + 4 * g) =
+                f32x4{dq_acc[mt][4 * i4], dq_acc[mt][4 * i4 + 1], dq_acc[mt][4 * i4 + 2],
+                      dq_acc[mt][4 * i4 + 3]} * a.scale;
+}
+
+template <bool BF16, int D, bool CAUSAL>
+hipError_t launch_bwd(BwdArgs a, hipStream_t stream) {
+    void* params[] = {(void*)&a};
+    const int64_t rows = (int64_t)a.BH * a.N;
+    const unsigned pre_grid = (unsigned)((rows + (256 / (D / 8)) - 1) / (256 / (D / 8)));
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_pre_kernel<BF16, D>),
+                                   dim3(pre_grid), dim3(256), params, 0, stream);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)(((a.N + kBwdRows - 1) / kBwdRows) * a.BH);
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<BF16, D, CAUSAL>),
+                        dim3(grid), dim3(64 * kBwdWaves), params, 0, stream);
+    if (e != hipSuccess) return e;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<BF16, D, CAUSAL>),
+                           dim3(grid), dim3(64 * kBwdWaves), params, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const float* o,
+                           const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                           float* workspace, int B, int H, int N, int D, bool causal, bool bf16,
+                           hipStream_t stream) {
+    BwdArgs a{};
+    a.q = static_cast<const u16*>(q);
+    a.k = static_cast<const u16*>(k);
+    a.v = static_cast<const u16*>(v);
+    a.o = o;
+    a.lse = lse;
+    a.dout = static_cast<const u16*>(dout);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.BH = B * H;
+    a.N = N;
+    a.dd = workspace;
+    a.lse2 = workspace + (int64_t)B * H * N;
+    a.scale_log2 = kLog2e / __builtin_sqrtf((float)D);
+    a.scale = 1.0f / __builtin_sqrtf((float)D);
+    if (D == 128) {
+        if (bf16)
+            return causal ? launch_bwd<true, 128, true>(a, stream) : launch_bwd<true, 128, false>(a, stream);
+        return causal ? launch_bwd<false, 128, true>(a, stream) : launch_bwd<false, 128, false>(a, stream);
+    }
+    if (bf16)
+        return causal ? launch_bwd<true, 64, true>(a, stream) : launch_bwd<true, 64, false>(a, stream);
+    return causal ? launch_bwd<false, 64, true>(a, stream) : launch_bwd<false, 64, false>(a, stream);
+}
+
+}  // namespace osc

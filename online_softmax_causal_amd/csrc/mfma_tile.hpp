@@ -96,6 +96,28 @@ __device__ __forceinline__ u32x4 tr16_b64x2(const u16* p0, const u16* p1) {
     return u32x4{(unsigned)a, (unsigned)(a >> 32), (unsigned)b, (unsigned)(b >> 32)};
 }
 
+// Offsets (16-bit elements, relative to an LDS tile of rows of D values in
+// the chunk_swizzle layout) of this lane's MFMA A-operand fragments:
+//   row_frag_offset: row `row` (lane % 32 of a 32-row block), the 8 values
+//     d = 16 ks + 8 (lane / 32) .. + 7 (one 16-wide step of the contraction
+//     over d);
+//   tr_frag_offset: one of the two ds_read_b64_tr_b16 reads (r = 0, 1) that
+//     give the transposed fragment X^T[d = 32 mt + lane % 32][16 rows of a
+//     group], the rows in the order of the 32x32 accumulator layout
+//     (8 (j / 4) + 4 (lane / 32) + j % 4 for slot j), relative to the group's
+//     first row.
+template <int D>
+__device__ __forceinline__ int row_frag_offset(int row, int ks, int lane) {
+    return row * D + (((2 * ks + (lane >> 5)) ^ chunk_swizzle<D>(row)) << 3);
+}
+
+template <int D>
+__device__ __forceinline__ int tr_frag_offset(int lane, int mt, int r) {
+    const int row = 4 * (lane >> 5) + ((lane >> 2) & 3) + 8 * r;
+    const int c = 4 * mt + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    return row * D + ((c ^ chunk_swizzle<D>(row)) << 3) + 4 * (lane & 1);
+}
+
 // Byte offset of an LDS location (what M0 and ds_* addresses use).
 __device__ __forceinline__ unsigned lds_offset(const void* p) {
     return (unsigned)(unsigned long long)((const __attribute__((address_space(3))) char*)p);
@@ -108,6 +130,14 @@ __device__ __forceinline__ unsigned lds_offset(const void* p) {
 // until the barrier after the matching wait_vmcnt.
 __device__ __forceinline__ void copy_to_lds16(const void* gbase, unsigned voff, void* lds_dst) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_offset(lds_dst)), "v"(voff), "s"(gbase)
+                 : "m0");
+}
+
+// The 4-byte form: lane i copies 4 bytes from gbase + voff to m0 + 4 * lane.
+__device__ __forceinline__ void copy_to_lds4(const void* gbase, unsigned voff, void* lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                  :
                  : "s"(lds_offset(lds_dst)), "v"(voff), "s"(gbase)
                  : "m0");

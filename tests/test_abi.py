@@ -196,6 +196,29 @@ def test_paged_decode_rejections():
     assert call_decode(splits=1, ws=None, ws_bytes=0) != 1  # no workspace needed: not a NULL error
 
 
+def call_bwd(q=BASE, k=BASE + 64 * MB, v=BASE + 128 * MB, o=BASE + 192 * MB, lse=BASE + 320 * MB,
+             do=BASE + 400 * MB, dq=BASE + 500 * MB, dk=BASE + 700 * MB, dv=BASE + 900 * MB,
+             B=1, H=2, N=4096, D=128, causal=1, dtype=0, ws=BASE + 1100 * MB, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = max(osc.attn_bwd_workspace(B, H, N), 0)
+    return osc.load().attn_bwd(q, k, v, o, lse, do, dq, dk, dv, B, H, N, D, causal, dtype, ws,
+                               ws_bytes, None)
+
+
+def test_attn_bwd_workspace_and_rejections():
+    assert osc.attn_bwd_workspace(1, 2, 4096) == 8 * 2 * 4096
+    assert osc.attn_bwd_workspace(0, 2, 4096) == -1
+    assert call_bwd(do=None) == 1
+    assert call_bwd(ws=None) == 1
+    assert call_bwd(N=0) == 2
+    assert call_bwd(D=96) == 3
+    assert call_bwd(dq=BASE + 500 * MB + 8) == 4
+    assert call_bwd(ws_bytes=8 * 2 * 4096 - 4) == 7
+    assert call_bwd(dk=BASE + 64 * MB) == 6              # dK on top of K
+    assert call_bwd(dv=BASE + 700 * MB + 1024) == 6      # dV inside dK
+    assert call_bwd(ws=BASE + 192 * MB) == 6             # workspace on O
+
+
 def call_softmax(x=BASE, y=BASE + 64 * MB, M=4, N=100):
     return osc.load().row_softmax(x, y, M, N, None)
 

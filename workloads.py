@@ -173,6 +173,20 @@ def gqa_inputs(B: int, H: int, Hkv: int, N: int, D: int, dtype: str, seed: int,
     return q.contiguous(), k.contiguous(), v.contiguous()
 
 
+def bwd_inputs(B: int, H: int, N: int, D: int, dtype: str, seed: int, sigma_qk: float = 1.0,
+               sigma_v: float = 1.0, sigma_do: float = 1.0):
+    """Q, K, V as attn_inputs, then dO [B,H,N,D] ~ N(0, sigma_do^2) drawn after V."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    shape = (B, H, N, D)
+    td = TORCH_DTYPE[dtype]
+    q = (torch.randn(shape, generator=g, dtype=torch.float32) * sigma_qk).to(td)
+    k = (torch.randn(shape, generator=g, dtype=torch.float32) * sigma_qk).to(td)
+    v = (torch.randn(shape, generator=g, dtype=torch.float32) * sigma_v).to(td)
+    do = (torch.randn(shape, generator=g, dtype=torch.float32) * sigma_do).to(td)
+    return q.contiguous(), k.contiguous(), v.contiguous(), do.contiguous()
+
+
 def workload_inputs(w: AttnWorkload):
     if w.Hkv is not None:
         return gqa_inputs(w.B, w.H, w.Hkv, w.N, w.D, w.dtype, w.seed, w.sigma_qk, w.sigma_v)
