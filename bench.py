@@ -19,7 +19,8 @@ One JSON line goes to stdout.  Besides the contract fields it carries:
   parity_sample max-abs error of the GPU output on those sampled rows;
   extra         the other configurations (C1, C2, C3, C5 attention; G1
                 grouped-query attention; S1 without and with the key split;
-                D1..D32 paged grouped-query decode at 1K..32K tokens;
+                D1..D32 paged grouped-query decode at 1K..32K tokens; C4 and
+                C5 backward;
                 R1, R2 row softmax), timed as the median of 7 group means of
                 back-to-back launches (FA page, section 8 method).
 Runs on one GPU only; --gpus above 1 exits with a message.
@@ -139,6 +140,27 @@ def extra_configs(dev):
                               "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4),
                               "workspace_bytes": need if entry != "attn_fwd" else 0}
     del q, k, v, o, lse, ws
+    # Backward of the headline workload (and of C5): algorithmic FLOP 2.5x the
+    # forward's (5 BHN^2D causal, 10 BHN^2D non-causal: the five N x N x D
+    # products dQ, dK, dV, dP and S); all three kernels inside the timed region.
+    for name in ("C4", "C5"):
+        w = workloads.ATTN[name]
+        q, k, v, do = (t.to(dev) for t in workloads.bwd_inputs(w.B, w.H, w.N, w.D, w.dtype, w.seed,
+                                                               w.sigma_qk, w.sigma_v))
+        o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        osc.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.D, w.causal, w.dtype)
+        dq, dk, dv = (torch.empty_like(o) for _ in range(3))
+        need = osc.attn_bwd_workspace(w.B, w.H, w.N)
+        ws = torch.empty((need // 4,), dtype=torch.float32, device=dev)
+        fn = lambda: osc.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, w.B, w.H, w.N, w.D, w.causal,
+                                  w.dtype, ws, need)
+        med, mn = time_groups(fn, stream)
+        tf = 2.5 * w.flops / (med * 1e-3) / 1e12
+        out[name + " bwd"] = {"workload": w.describe().replace("fwd", "bwd"), "entry": "attn_bwd",
+                              "ms": round(med, 5), "ms_min": round(mn, 5), "tflops": round(tf, 2),
+                              "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+        del q, k, v, do, o, lse, dq, dk, dv, ws
     # Paged grouped-query decode (KV page, section 8 shapes), automatic split;
     # attention kernel and merge inside the timed region.  HBM-bound: GB/s of
     # algorithmic bytes (K and V of every cached token once, q, o, lse).
@@ -255,6 +277,28 @@ def profile_decode(launches=30):
     print("decode launches:", launches, w.describe(), "algorithmic bytes per launch", w.bytes)
 
 
+def profile_bwd(launches=10):
+    """One forward, then `launches` backward calls of the headline workload (for rocprofv3)."""
+    import torch
+    import online_softmax_causal_amd as osc
+    import workloads
+    dev = torch.device("cuda:0")
+    w = workloads.ATTN["C4"]
+    q, k, v, do = (t.to(dev) for t in workloads.bwd_inputs(w.B, w.H, w.N, w.D, w.dtype, w.seed))
+    o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    osc.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.D, w.causal, w.dtype)
+    dq, dk, dv = (torch.empty_like(o) for _ in range(3))
+    need = osc.attn_bwd_workspace(w.B, w.H, w.N)
+    ws = torch.empty((need // 4,), dtype=torch.float32, device=dev)
+    for _ in range(launches):
+        osc.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, w.B, w.H, w.N, w.D, w.causal, w.dtype, ws,
+                     need)
+    torch.cuda.synchronize()
+    print("backward launches:", launches, w.describe().replace("fwd", "bwd"),
+          "algorithmic FLOP per launch", 2.5 * w.flops)
+
+
 def _pmc_rows(path):
     import csv
     import glob
@@ -321,6 +365,43 @@ def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
     print(text)
 
 
+def summarize_sq(dirs, out_path, cmds):
+    """Write profiles/attn_fwd_C4_sq_counters.txt from rocprofv3 --pmc SQ passes of --profile-pass."""
+    import statistics
+    vals = {}
+    for d in dirs:
+        rows = _pmc_rows(d)
+        for r in rows:
+            if "attn_fwd_kernel" in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in vals.items()}
+    simds, xcds = 256 * 4, 8
+    lines = ["attn_fwd_kernel, causal fp16 B1 H32 N8192 D128: SQ counters per dispatch (rocprofv3 --pmc)",
+             "", "commands (from the repository root, TMPDIR=/tmp):"]
+    lines += ["  " + c for c in cmds]
+    lines += ["", "counter | per dispatch (3 dispatches) | median"]
+    for k in sorted(vals):
+        lines.append("%s | %s | %.5g" % (k, ", ".join("%.5g" % x for x in vals[k]), med[k]))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
+        cycles = med["GRBM_GUI_ACTIVE"] / xcds
+        util = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cycles)
+        lines += ["",
+                  "GPU cycles per dispatch = GRBM_GUI_ACTIVE / 8 XCDs = %.4g" % cycles,
+                  "MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) = %.3f" % util]
+    if "SQ_INSTS_MFMA" in med and "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+        lines.append("busy cycles per MFMA instruction = %.2f (v_mfma_f32_32x32x16: 32)"
+                     % (med["SQ_VALU_MFMA_BUSY_CYCLES"] / med["SQ_INSTS_MFMA"]))
+    wave_tiles = 32 * 4 * 528 * 8   # heads x (sum over query tiles of 64-key tiles) x waves
+    for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+        if k in med:
+            lines.append("%s per wave per 64-key tile = %.1f" % (k, med[k] / wave_tiles))
+    lines.append("kernel_source_sha256_16: %s" % kernel_source_hash())
+    lines.append("")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def summarize_trace(trace_dir, out_path, cmd, last):
     """Write a kernel-duration summary from a rocprofv3 --kernel-trace --stats csv run.
 
@@ -347,7 +428,8 @@ def summarize_trace(trace_dir, out_path, cmd, last):
                 (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     lines.append("")
     for name, d in durs.items():
-        if any(k in name for k in ("attn_fwd_kernel", "softmax", "paged_decode", "splitkv_merge")):
+        if any(k in name for k in ("attn_fwd_kernel", "softmax", "paged_decode", "splitkv_merge",
+                                   "attn_bwd")):
             d.sort()
             tail = [x[1] for x in d[-last:]]
             lines.append("%s: mean of the last %d launches (the timed steps) %.2f us" % (
@@ -373,13 +455,20 @@ def main():
                     help="run the fixed launch sequence the counter passes profile")
     ap.add_argument("--profile-decode", action="store_true",
                     help="only launch the 32K-context paged decode 30 times (for rocprofv3)")
+    ap.add_argument("--profile-bwd", action="store_true",
+                    help="only run the headline workload's backward 10 times (for rocprofv3)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DIR")
     ap.add_argument("--trace-last", type=int, default=20)
     ap.add_argument("--cmd", default="")
     ap.add_argument("--cmd-fetch", default="")
     ap.add_argument("--cmd-write", default="")
     args = ap.parse_args()
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, os.path.join(ROOT, "profiles", "attn_fwd_C4_sq_counters.txt"),
+                     args.cmd.split(" ;; "))
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.cmd, args.trace_last)
         return
@@ -392,6 +481,9 @@ def main():
         return
     if args.profile_decode:
         profile_decode()
+        return
+    if args.profile_bwd:
+        profile_bwd()
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
