@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
@@ -143,6 +144,61 @@ attn_bwd_pre_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// acc[kb] += rows 32 kb .. 32 kb + 31 of `tile` (lane row lane % 32) times the
+// B-operand fragments bf over d, for kb < KB: KB * KS MFMAs whose A fragments
+// stream through a 4-deep register ring (held by scheduling groups, so each
+// LDS read is issued four fragments ahead of its use).
+template <bool BF16, int D, int KB>
+__device__ __forceinline__ void rows_times(const u16* tile, const int (&rfo)[D / 16],
+                                           const u32x4 (&bf)[D / 16], f32x16 (&acc)[KB]) {
+    using M = Mma<BF16>;
+    constexpr int KS = D / 16, NF = KB * KS;
+    auto frag = [&](int f) {
+        return *reinterpret_cast<const u32x4*>(tile + (f % KB) * 32 * D + rfo[f / KB]);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 ring[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) ring[f] = frag(f);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const u32x4 x = ring[f & 3];
+        if (f + 4 < NF) ring[f & 3] = frag(f + 4);
+        acc[f % KB] = M::run(x, bf[f / KB], acc[f % KB]);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+#pragma unroll
+    for (int f = 0; f < NF - 4; ++f) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// acc[mt] += X^T[d = 32 mt + ..][16 rows of group u] * bf[u] over the NU
+// 16-row groups of `tile`: 2 * NU * MT transpose reads through a 4-fragment
+// ring.  X^T is read in the accumulator's row order (tr_frag_offset).
+template <bool BF16, int D, int NU>
+__device__ __forceinline__ void trans_times(const u16* tile, const int (&tfo)[D / 32][2],
+                                            const u32x4 (&bf)[NU], f32x16 (&acc)[D / 32]) {
+    using M = Mma<BF16>;
+    constexpr int MT = D / 32, NF = NU * MT;
+    auto frag = [&](int f) {
+        const u16* base = tile + (f / MT) * 16 * D;
+        return tr16_b64x2(base + tfo[f % MT][0], base + tfo[f % MT][1]);
+    };
+    u32x4 ring[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) ring[f] = frag(f);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const u32x4 x = ring[f & 3];
+        if (f + 4 < NF) ring[f & 3] = frag(f + 4);
+        acc[f % MT] = M::run(x, bf[f / MT], acc[f % MT]);
+    }
+}
+
 template <bool BF16, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
 attn_bwd_dkdv_kernel(BwdArgs a) {
@@ -206,7 +262,9 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
             copy_to_lds4(src, (unsigned)(row * 4), st + 2 * TILE + w * 2 * kBwdTile);
         }
     };
-    auto wait_next = [&](int it) {  // tile it+1 landed for this wave
+    // Tile it+1 complete for this wave (tile it+2 may stay in flight), then
+    // for all waves.
+    auto wait_next = [&](int it) {
         if (it + 2 < nqt) {
             if (w < 2)
                 wait_vmcnt<2 * LPM + 1>();
@@ -217,6 +275,58 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
         }
         __syncthreads();
     };
+
+    // One 32-query block at row qb of a staged tile: S = Q K^T and dP = dO V^T
+    // (lane (col, g) holds query rows qb + 8(e/4) + 4g + e%4 of key `key`),
+    // P from the saved LSE, dS = P (dP - D), then dV^T += dO^T P and
+    // dK^T += Q^T dS.  MASKED zeroes P where key > query (causal) or the
+    // query row is past N.
+    auto block = [&](const u16* st, int b, int qb, auto masked_tag) {
+        const u16* qt = st + 32 * b * D;
+        const u16* dot = st + TILE + 32 * b * D;
+        const float* l2t = reinterpret_cast<const float*>(st + 2 * TILE) + 32 * b;
+        const float* ddt = l2t + kBwdTile;
+        f32x16 s[1] = {f32x16{}}, dp[1] = {f32x16{}};
+        rows_times<BF16, D, 1>(qt, rfo, kf, s);
+        rows_times<BF16, D, 1>(dot, rfo, vf, dp);
+        int lo = 0, hi = 32;
+        if constexpr (decltype(masked_tag)::value) {
+            // masked iff offset e' = 8(e/4) + e%4 is < key - qb - 4g (causal)
+            // or >= N - qb - 4g (rows past N)
+            lo = CAUSAL ? key - qb - 4 * g : -1;
+            hi = N - qb - 4 * g;
+        }
+        u32x4 pf[2], dsf[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float p[8], ds[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int j4 = 2 * u + h;
+                const f32x4 l2 = *reinterpret_cast<const f32x4*>(l2t + 8 * j4 + 4 * g);
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(ddt + 8 * j4 + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * j4 + i;
+                    float pe = fast_exp2(fmaf(s[0][e], a.scale_log2, -l2[i]));
+                    if constexpr (decltype(masked_tag)::value) {
+                        const int off = 8 * j4 + i;
+                        pe = (off < lo || off >= hi) ? 0.0f : pe;
+                    }
+                    p[4 * h + i] = pe;
+                    ds[4 * h + i] = pe * (dp[0][e] - dd[i]);
+                }
+            }
+            pf[u] = u32x4{M::pack(p[0], p[1]), M::pack(p[2], p[3]), M::pack(p[4], p[5]),
+                          M::pack(p[6], p[7])};
+            dsf[u] = u32x4{M::pack(ds[0], ds[1]), M::pack(ds[2], ds[3]), M::pack(ds[4], ds[5]),
+                           M::pack(ds[6], ds[7])};
+        }
+        trans_times<BF16, D, 2>(dot, tfo, pf, dv_acc);
+        trans_times<BF16, D, 2>(qt, tfo, dsf, dk_acc);
+    };
+    std::integral_constant<bool, false> plain;
+    std::integral_constant<bool, true> masked;
 
     issue(qt0);
     issue(qt0 + 1);
@@ -232,59 +342,15 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 
     for (int it = qt0; it < nqt; ++it) {
         issue(it + 2);
-        const u16* qt = stage(it);
-        const u16* dot = qt + TILE;
-        const float* l2t = reinterpret_cast<const float*>(qt + 2 * TILE);
-        const float* ddt = l2t + kBwdTile;
+        const u16* st = stage(it);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int qb = it * kBwdTile + 32 * b;  // first query row of the block
             if (qb >= N || (CAUSAL && qb + 31 < kw)) continue;
-            f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s = M::run(*reinterpret_cast<const u32x4*>(qt + 32 * b * D + rfo[ks]), kf[ks], s);
-                dp = M::run(*reinterpret_cast<const u32x4*>(dot + 32 * b * D + rfo[ks]), vf[ks], dp);
-            }
-            // Lane (col, g) holds query rows qb + 8(e/4) + 4g + e%4 of key `key`.
-            const bool edge = (CAUSAL && qb < kw + 31) || qb + 32 > N;
-            float p[16], ds[16];
-#pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-                const f32x4 l2 = *reinterpret_cast<const f32x4*>(l2t + 32 * b + 8 * j4 + 4 * g);
-                const f32x4 dd = *reinterpret_cast<const f32x4*>(ddt + 32 * b + 8 * j4 + 4 * g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = 4 * j4 + i;
-                    float pe = fast_exp2(fmaf(s[e], a.scale_log2, -l2[i]));
-                    if (edge) {
-                        const int qrow = qb + 8 * j4 + 4 * g + i;
-                        if ((CAUSAL && key > qrow) || qrow >= N) pe = 0.0f;
-                    }
-                    p[e] = pe;
-                    ds[e] = pe * (dp[e] - dd[i]);
-                }
-            }
-            u32x4 pf[2], dsf[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                pf[u] = u32x4{M::pack(p[8 * u], p[8 * u + 1]), M::pack(p[8 * u + 2], p[8 * u + 3]),
-                              M::pack(p[8 * u + 4], p[8 * u + 5]), M::pack(p[8 * u + 6], p[8 * u + 7])};
-                dsf[u] = u32x4{M::pack(ds[8 * u], ds[8 * u + 1]), M::pack(ds[8 * u + 2], ds[8 * u + 3]),
-                               M::pack(ds[8 * u + 4], ds[8 * u + 5]), M::pack(ds[8 * u + 6], ds[8 * u + 7])};
-            }
-            // dV^T += dO^T P and dK^T += Q^T dS: A operands read transposed,
-            // 16 query rows per step, in the accumulator's row order.
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const u16* dog = dot + (32 * b + 16 * u) * D;
-                const u16* qg = qt + (32 * b + 16 * u) * D;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    dv_acc[mt] = M::run(tr16_b64x2(dog + tfo[mt][0], dog + tfo[mt][1]), pf[u], dv_acc[mt]);
-                    dk_acc[mt] = M::run(tr16_b64x2(qg + tfo[mt][0], qg + tfo[mt][1]), dsf[u], dk_acc[mt]);
-                }
-            }
+            if ((CAUSAL && qb < kw + 31) || qb + 32 > N)
+                block(st, b, qb, masked);
+            else
+                block(st, b, qb, plain);
         }
         wait_next(it);
     }
@@ -352,7 +418,8 @@ attn_bwd_dq_kernel(BwdArgs a) {
 
     const int kv_end = CAUSAL ? min(t * kBwdRows + kBwdRows, N) : N;
     const int ntiles = (kv_end + kBwdTile - 1) / kBwdTile;
-    // This wave's last key tile (none if its rows are past N).
+    // This wave's last key tile, its diagonal or ragged-tail tile (the only
+    // one that can need masking); -1 if its rows are past N.
     const int last = row0 >= N ? -1 : min(ntiles - 1, CAUSAL ? (row0 + 31) / kBwdTile : ntiles - 1);
     auto stage = [&](int it) { return lds + (it % kBwdStages) * STAGE; };
     auto issue = [&](int it) {
@@ -361,6 +428,49 @@ attn_bwd_dq_kernel(BwdArgs a) {
         copy_tile<D>(a.k + head * D, st, it * kBwdTile, N, w, lane);
         copy_tile<D>(a.v + head * D, st + TILE, it * kBwdTile, N, w, lane);
     };
+    auto finish = [&](int it) {
+        if (it + 2 < ntiles)
+            wait_vmcnt<2 * LPM>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+    };
+    // One 64-key tile: S^T = K Q^T and dP^T = V dO^T (lane (col, g) holds
+    // keys 32 kb + 8(e/4) + 4g + e%4 of query `row`), P^T from the saved LSE,
+    // dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.  MASKED zeroes keys after the
+    // query (causal) or past N.
+    auto tile = [&](int it, auto masked_tag) {
+        const u16* kt = stage(it);
+        const u16* vt = kt + TILE;
+        f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+        rows_times<BF16, D, 2>(kt, rfo, qf, s);
+        rows_times<BF16, D, 2>(vt, rfo, dof, dp);
+        const int key0 = it * kBwdTile;
+        int lim = 1 << 30;
+        if constexpr (decltype(masked_tag)::value)
+            lim = min(CAUSAL ? row - key0 : (1 << 30), N - 1 - key0) - 4 * g;
+        u32x4 dsf[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kb = u >> 1, h = (u & 1) * 8;
+            float ds[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int e = h + jj;
+                float pe = fast_exp2(fmaf(s[kb][e], a.scale_log2, -l2));
+                if constexpr (decltype(masked_tag)::value) {
+                    const int c = 32 * kb + 8 * (e >> 2) + (e & 3);
+                    pe = c > lim ? 0.0f : pe;
+                }
+                ds[jj] = pe * (dp[kb][e] - dd);
+            }
+            dsf[u] = u32x4{M::pack(ds[0], ds[1]), M::pack(ds[2], ds[3]), M::pack(ds[4], ds[5]),
+                           M::pack(ds[6], ds[7])};
+        }
+        trans_times<BF16, D, 4>(kt, tfo, dsf, dq_acc);
+    };
+    std::integral_constant<bool, false> plain;
+    std::integral_constant<bool, true> masked;
 
     issue(0);
     issue(1);
@@ -370,55 +480,21 @@ attn_bwd_dq_kernel(BwdArgs a) {
         wait_vmcnt<0>();
     __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
+    int it = 0;
+    for (; it < last; ++it) {
         issue(it + 2);
-        if (it <= last) {
-            const u16* kt = stage(it);
-            const u16* vt = kt + TILE;
-            // S^T and dP^T for keys 32 kb + (accumulator rows): lane (col, g)
-            // holds keys 32 kb + 8 (e / 4) + 4 g + e % 4 of query `row`.
-            f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    s[kb] = M::run(*reinterpret_cast<const u32x4*>(kt + 32 * kb * D + rfo[ks]), qf[ks], s[kb]);
-                    dp[kb] = M::run(*reinterpret_cast<const u32x4*>(vt + 32 * kb * D + rfo[ks]), dof[ks], dp[kb]);
-                }
-            const int key0 = it * kBwdTile;
-            const bool edge = (CAUSAL && key0 + kBwdTile - 1 > row0) || key0 + kBwdTile > N;
-            u32x4 dsf[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int kb = u >> 1, h = (u & 1) * 8;
-                float ds[8];
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int e = h + jj;
-                    float pe = fast_exp2(fmaf(s[kb][e], a.scale_log2, -l2));
-                    if (edge) {
-                        const int kidx = key0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-                        if ((CAUSAL && kidx > row) || kidx >= N) pe = 0.0f;
-                    }
-                    ds[jj] = pe * (dp[kb][e] - dd);
-                }
-                dsf[u] = u32x4{M::pack(ds[0], ds[1]), M::pack(ds[2], ds[3]), M::pack(ds[4], ds[5]),
-                               M::pack(ds[6], ds[7])};
-            }
-            // dQ^T += K^T dS^T: K^T read transposed, 16 keys per step.
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const u16* kg = kt + 16 * u * D;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    dq_acc[mt] = M::run(tr16_b64x2(kg + tfo[mt][0], kg + tfo[mt][1]), dsf[u], dq_acc[mt]);
-            }
-        }
-        if (it + 2 < ntiles)
-            wait_vmcnt<2 * LPM>();
-        else
-            wait_vmcnt<0>();
-        __syncthreads();
+        tile(it, plain);
+        finish(it);
+    }
+    if (it == last) {
+        issue(it + 2);
+        tile(it, masked);
+        finish(it);
+        ++it;
+    }
+    for (; it < ntiles; ++it) {
+        issue(it + 2);
+        finish(it);
     }
 
     if (row >= N) return;
