@@ -83,11 +83,11 @@ __device__ __forceinline__ void bwd_work(int bid, int BH, int ntiles, bool rever
 // Copy rows [row0, row0 + 64) of a [N, D] 16-bit matrix into an LDS tile
 // (chunk-swizzled rows); the four waves share the 1 KiB blocks.  Rows past N
 // repeat row N - 1 (finite data; the kernels mask them).
-template <int D>
+template <int D, int NW = kBwdWaves>
 __device__ __forceinline__ void copy_tile(const u16* src, u16* dst, int row0, int N, int w,
                                           int lane) {
     constexpr int CPR = D / 8, RPB = 1024 / (2 * D);
-    constexpr int BPW = kBwdTile / RPB / kBwdWaves;
+    constexpr int BPW = kBwdTile / RPB / NW;
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
         const int blk = w * BPW + j;
@@ -98,10 +98,13 @@ __device__ __forceinline__ void copy_tile(const u16* src, u16* dst, int row0, in
     }
 }
 
-template <int D>
+template <int D, int NW = kBwdWaves>
 constexpr int copies_per_matrix() {
-    return kBwdTile / (1024 / (2 * D)) / kBwdWaves;
+    return kBwdTile / (1024 / (2 * D)) / NW;
 }
+
+constexpr int kDqWaves = 8;                  // dQ kernel: two waves per SIMD
+constexpr int kDqRows = 32 * kDqWaves;       // query rows per dQ workgroup
 
 // One 16-bit value (low bits of b) as FP32, exactly.
 template <bool BF16>
@@ -375,24 +378,24 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 template <bool BF16, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(64 * kDqWaves, 1)
 attn_bwd_dq_kernel(BwdArgs a) {
     using M = Mma<BF16>;
     constexpr int KS = D / 16, MT = D / 32;
     constexpr int TILE = kBwdTile * D;
     constexpr int STAGE = 2 * TILE;  // K, V
-    constexpr int LPM = copies_per_matrix<D>();
+    constexpr int LPM = copies_per_matrix<D, kDqWaves>();
     __shared__ __attribute__((aligned(1024))) u16 lds[kBwdStages * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31, g = lane >> 5;
     const int N = a.N;
-    const int nq = (N + kBwdRows - 1) / kBwdRows;
+    const int nq = (N + kDqRows - 1) / kDqRows;
     int t, bh;
     bwd_work(blockIdx.x, a.BH, nq, CAUSAL, &t, &bh);
     const int64_t head = (int64_t)bh * N;
-    const int row0 = t * kBwdRows + 32 * w;  // first query row of this wave
+    const int row0 = t * kDqRows + 32 * w;  // first query row of this wave
     const int row = row0 + col;
 
     u32x4 qf[KS], dof[KS];
@@ -416,7 +419,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) tfo[mt][r] = tr_frag_offset<D>(lane, mt, r);
 
-    const int kv_end = CAUSAL ? min(t * kBwdRows + kBwdRows, N) : N;
+    const int kv_end = CAUSAL ? min(t * kDqRows + kDqRows, N) : N;
     const int ntiles = (kv_end + kBwdTile - 1) / kBwdTile;
     // This wave's last key tile, its diagonal or ragged-tail tile (the only
     // one that can need masking); -1 if its rows are past N.
@@ -425,8 +428,8 @@ attn_bwd_dq_kernel(BwdArgs a) {
     auto issue = [&](int it) {
         if (it >= ntiles) return;
         u16* st = stage(it);
-        copy_tile<D>(a.k + head * D, st, it * kBwdTile, N, w, lane);
-        copy_tile<D>(a.v + head * D, st + TILE, it * kBwdTile, N, w, lane);
+        copy_tile<D, kDqWaves>(a.k + head * D, st, it * kBwdTile, N, w, lane);
+        copy_tile<D, kDqWaves>(a.v + head * D, st + TILE, it * kBwdTile, N, w, lane);
     };
     auto finish = [&](int it) {
         if (it + 2 < ntiles)
@@ -439,35 +442,40 @@ attn_bwd_dq_kernel(BwdArgs a) {
     // keys 32 kb + 8(e/4) + 4g + e%4 of query `row`), P^T from the saved LSE,
     // dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.  MASKED zeroes keys after the
     // query (causal) or past N.
+    // The tile is taken as two halves of 32 keys, to keep the live registers
+    // within two waves per SIMD.
     auto tile = [&](int it, auto masked_tag) {
         const u16* kt = stage(it);
         const u16* vt = kt + TILE;
-        f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-        rows_times<BF16, D, 2>(kt, rfo, qf, s);
-        rows_times<BF16, D, 2>(vt, rfo, dof, dp);
         const int key0 = it * kBwdTile;
         int lim = 1 << 30;
         if constexpr (decltype(masked_tag)::value)
             lim = min(CAUSAL ? row - key0 : (1 << 30), N - 1 - key0) - 4 * g;
-        u32x4 dsf[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int kb = u >> 1, h = (u & 1) * 8;
-            float ds[8];
+        for (int half = 0; half < 2; ++half) {
+            const u16* kh = kt + 32 * half * D;
+            f32x16 s[1] = {f32x16{}}, dp[1] = {f32x16{}};
+            rows_times<BF16, D, 1>(kh, rfo, qf, s);
+            rows_times<BF16, D, 1>(vt + 32 * half * D, rfo, dof, dp);
+            u32x4 dsf[2];
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int e = h + jj;
-                float pe = fast_exp2(fmaf(s[kb][e], a.scale_log2, -l2));
-                if constexpr (decltype(masked_tag)::value) {
-                    const int c = 32 * kb + 8 * (e >> 2) + (e & 3);
-                    pe = c > lim ? 0.0f : pe;
+            for (int u = 0; u < 2; ++u) {
+                float ds[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int e = 8 * u + jj;
+                    float pe = fast_exp2(fmaf(s[0][e], a.scale_log2, -l2));
+                    if constexpr (decltype(masked_tag)::value) {
+                        const int c = 32 * half + 8 * (e >> 2) + (e & 3);
+                        pe = c > lim ? 0.0f : pe;
+                    }
+                    ds[jj] = pe * (dp[0][e] - dd);
                 }
-                ds[jj] = pe * (dp[kb][e] - dd);
+                dsf[u] = u32x4{M::pack(ds[0], ds[1]), M::pack(ds[2], ds[3]), M::pack(ds[4], ds[5]),
+                               M::pack(ds[6], ds[7])};
             }
-            dsf[u] = u32x4{M::pack(ds[0], ds[1]), M::pack(ds[2], ds[3]), M::pack(ds[4], ds[5]),
-                           M::pack(ds[6], ds[7])};
+            trans_times<BF16, D, 2>(kh, tfo, dsf, dq_acc);
         }
-        trans_times<BF16, D, 4>(kt, tfo, dsf, dq_acc);
     };
     std::integral_constant<bool, false> plain;
     std::integral_constant<bool, true> masked;
@@ -520,8 +528,9 @@ hipError_t launch_bwd(BwdArgs a, hipStream_t stream) {
     e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<BF16, D, CAUSAL>),
                         dim3(grid), dim3(64 * kBwdWaves), params, 0, stream);
     if (e != hipSuccess) return e;
+    const unsigned dq_grid = (unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.BH);
     return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<BF16, D, CAUSAL>),
-                           dim3(grid), dim3(64 * kBwdWaves), params, 0, stream);
+                           dim3(dq_grid), dim3(64 * kDqWaves), params, 0, stream);
 }
 
 }  // namespace
