@@ -14,13 +14,15 @@
 // Three kernels, all on one stream:
 //   attn_bwd_pre_kernel   D_i and the base-2 log-sum-exp lse_i * log2(e) of
 //                         every row, into the caller's workspace (HBM-bound);
-//   attn_bwd_dkdv_kernel  key-major: a workgroup keeps 128 keys (32 per wave)
-//                         of K and V in registers and streams 64-row tiles of
+//   attn_bwd_dkdv_kernel  key-major: a workgroup keeps 32 keys per wave (4
+//                         waves at D = 128, 8 at D = 64) of K and V in
+//                         registers and streams 64-row tiles of
 //                         Q and dO (with D and lse of those rows) through LDS;
 //                         dV^T += dO^T P and dK^T += Q^T dS on the MFMA;
-//   attn_bwd_dq_kernel    query-major, like the forward kernel: a workgroup
-//                         keeps 128 query rows of Q and dO in registers and
-//                         streams 64-key tiles of K and V; dQ^T += K^T dS^T.
+//   attn_bwd_dq_kernel    query-major, like the forward kernel: a workgroup of
+//                         8 waves (two per SIMD) keeps 256 query rows of Q and
+//                         dO in registers and streams 64-key tiles of K and V,
+//                         taken 32 keys at a time; dQ^T += K^T dS^T.
 // Splitting dQ from dK/dV recomputes S and dP once more but needs no atomic
 // accumulation, so the result is deterministic.  P and dS are rounded RNE to
 // the input dtype as MFMA operands; every accumulation is FP32.
@@ -103,6 +105,12 @@ constexpr int copies_per_matrix() {
     return kBwdTile / (1024 / (2 * D)) / NW;
 }
 
+// dK/dV kernel waves: two per SIMD where K, V and both accumulators fit 256
+// registers (D = 64); one per SIMD at D = 128 (8 waves spill heavily there).
+template <int D>
+constexpr int dkdv_waves() {
+    return D == 128 ? 4 : 8;
+}
 constexpr int kDqWaves = 8;                  // dQ kernel: two waves per SIMD
 constexpr int kDqRows = 32 * kDqWaves;       // query rows per dQ workgroup
 
@@ -203,24 +211,26 @@ __device__ __forceinline__ void trans_times(const u16* tile, const int (&tfo)[D 
 }
 
 template <bool BF16, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(64 * dkdv_waves<D>(), 1)
 attn_bwd_dkdv_kernel(BwdArgs a) {
+    constexpr int kDkdvWaves = dkdv_waves<D>();
+    constexpr int kDkdvRows = 32 * kDkdvWaves;
     using M = Mma<BF16>;
     constexpr int KS = D / 16, MT = D / 32;
     constexpr int TILE = kBwdTile * D;
     constexpr int STAGE = 2 * TILE + 2 * kBwdTile * 2;  // Q, dO (16-bit), lse2, D (FP32)
-    constexpr int LPM = copies_per_matrix<D>();
+    constexpr int LPM = copies_per_matrix<D, kDkdvWaves>();
     __shared__ __attribute__((aligned(1024))) u16 lds[kBwdStages * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31, g = lane >> 5;
     const int N = a.N;
-    const int nkt = (N + kBwdRows - 1) / kBwdRows;
+    const int nkt = (N + kDkdvRows - 1) / kDkdvRows;
     int kt, bh;
     bwd_work(blockIdx.x, a.BH, nkt, false, &kt, &bh);
     const int64_t head = (int64_t)bh * N;
-    const int kw = kt * kBwdRows + 32 * w;  // first key of this wave
+    const int kw = kt * kDkdvRows + 32 * w;  // first key of this wave
     const int key = kw + col;
 
     // K^T and V^T fragments (B operands): lane (col, g) holds key `key`,
@@ -250,15 +260,15 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     // Query tiles: with causal masking only rows at or after the workgroup's
     // first key contribute.
     const int nqt = (N + kBwdTile - 1) / kBwdTile;
-    const int qt0 = CAUSAL ? (kt * kBwdRows) / kBwdTile : 0;
+    const int qt0 = CAUSAL ? (kt * kDkdvRows) / kBwdTile : 0;
     auto stage = [&](int it) { return lds + (it % kBwdStages) * STAGE; };
     // Waves 0 and 1 also copy the tile's lse2 and D rows (one 4-byte copy each).
     auto issue = [&](int it) {
         if (it >= nqt) return;
         u16* st = stage(it);
         const int r0 = it * kBwdTile;
-        copy_tile<D>(a.q + head * D, st, r0, N, w, lane);
-        copy_tile<D>(a.dout + head * D, st + TILE, r0, N, w, lane);
+        copy_tile<D, kDkdvWaves>(a.q + head * D, st, r0, N, w, lane);
+        copy_tile<D, kDkdvWaves>(a.dout + head * D, st + TILE, r0, N, w, lane);
         if (w < 2) {
             const int row = min(r0 + lane, N - 1);
             const float* src = w == 0 ? a.lse2 + head : a.dd + head;
@@ -524,9 +534,10 @@ hipError_t launch_bwd(BwdArgs a, hipStream_t stream) {
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_pre_kernel<BF16, D>),
                                    dim3(pre_grid), dim3(256), params, 0, stream);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)(((a.N + kBwdRows - 1) / kBwdRows) * a.BH);
+    constexpr int kv_rows = 32 * dkdv_waves<D>();
+    const unsigned grid = (unsigned)(((a.N + kv_rows - 1) / kv_rows) * a.BH);
     e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<BF16, D, CAUSAL>),
-                        dim3(grid), dim3(64 * kBwdWaves), params, 0, stream);
+                        dim3(grid), dim3(64 * dkdv_waves<D>()), params, 0, stream);
     if (e != hipSuccess) return e;
     const unsigned dq_grid = (unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.BH);
     return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<BF16, D, CAUSAL>),
