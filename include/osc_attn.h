@@ -1,8 +1,8 @@
 /*
- * osc_attn.h - C ABI of the MI355X (gfx950) attention-forward and row-softmax
- * library (libosc_attn.so).
+ * osc_attn.h - C ABI of the MI355X (gfx950) attention library
+ * (libosc_attn.so).
  *
- * Two operations, both from the reference pages:
+ * Operations, all from the reference pages:
  *
  *   attn_fwd     exact scaled-dot-product attention forward,
  *                O = softmax(Q K^T / sqrt(D) + M) V, with M the causal mask
@@ -13,6 +13,11 @@
  *                running sum l, unnormalised FP32 output rescaled per K/V
  *                tile), which reaches the same result as the plain definition
  *                up to floating-point rounding.
+ *   attn_fwd_gqa      the same with fewer K/V heads than query heads.
+ *   attn_fwd_splitkv  the same with every head's keys split into segments
+ *                whose partial states are merged afterwards.
+ *   paged_decode one decode step over a paged K/V cache.
+ *   attn_bwd     gradients of attn_fwd with respect to q, k and v.
  *
  *   row_softmax  y = softmax(x) along each row of an FP32 matrix, computed
  *                with the online (m, d) recurrence and two-level merge of the
@@ -21,7 +26,8 @@
  *
  * Conventions (all entry points):
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
- *     allocates no memory, keeps no state between calls and never synchronises.
+ *     allocates no memory (scratch space comes from a caller's workspace
+ *     argument), keeps no state between calls and never synchronises.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns at once.  Completion is observed with the caller's own stream or
  *     event synchronisation; a fault during execution surfaces there.
@@ -217,6 +223,54 @@ attn_status_t paged_decode(const void *q, const void *cache, const int32_t *bloc
  */
 int64_t paged_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
                                int64_t max_pages, int num_splits);
+
+/*
+ * attn_bwd - gradients of the attention forward (attn_fwd) with respect to
+ * q, k and v, for an upstream gradient dout = dL/dO.
+ *
+ * The pages define only the forward; the FA page (section 7) keeps the
+ * log-sum-exp so that a backward pass can rebuild the softmax weights without
+ * storing them.  This call does that: with s_ij = q_i . k_j / sqrt(D) over
+ * the visible keys and p_ij = exp(s_ij - lse_i),
+ *     dV_j = sum_i p_ij dO_i,
+ *     dP_ij = dO_i . v_j,   Delta_i = dO_i . O_i,   dS_ij = p_ij (dP_ij - Delta_i),
+ *     dQ_i = sum_j dS_ij k_j / sqrt(D),   dK_j = sum_i dS_ij q_i / sqrt(D),
+ * which is the derivative of the section 1 definition (Delta_i equals
+ * sum_j p_ij dP_ij because each softmax row sums to one).  Every output
+ * element is written by one workgroup in a fixed order: no atomics, and the
+ * result is bit-for-bit repeatable.
+ *
+ *   q, k, v  [B, H, N, D] of `dtype`, 16-byte aligned: the forward's inputs.
+ *   o        [B, H, N, D] FP32, 16-byte aligned: attn_fwd's output for them.
+ *   lse      [B, H, N] FP32, 4-byte aligned: attn_fwd's log-sum-exp.
+ *   dout     [B, H, N, D] of `dtype`, 16-byte aligned: dL/dO.
+ *   dq, dk, dv  [B, H, N, D] FP32 outputs, 16-byte aligned.
+ *   B, H, N, D, causal, dtype  as for attn_fwd (D 64 or 128; K/V heads
+ *            equal to query heads).
+ *   workspace  device buffer owned by the caller, 16-byte aligned, of at
+ *            least attn_bwd_workspace(B, H, N) bytes (8 per row): it receives
+ *            Delta and lse in base 2 before the gradient kernels read them.
+ *            Its contents on entry do not matter and are undefined after the
+ *            call.  Two calls that run at the same time need separate ones.
+ *   workspace_bytes  size of `workspace`; too small: ATTN_ERR_WORKSPACE.
+ *   stream   HIP stream to enqueue on (three kernels, in order).
+ *
+ * Errors: NULL pointer ATTN_ERR_NULL, sizes and limits as for attn_fwd,
+ * alignment ATTN_ERR_ALIGN; dq, dk, dv and the workspace must not overlap
+ * any input or each other (ATTN_ERR_ALIAS).  o and lse are used as given: a
+ * pair that does not come from attn_fwd on the same q, k, v gives gradients
+ * of nothing in particular, without an error.
+ */
+attn_status_t attn_bwd(const void *q, const void *k, const void *v, const float *o,
+                       const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                       int64_t B, int64_t H, int64_t N, int64_t D, int causal, attn_dtype_t dtype,
+                       void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_bwd_workspace - bytes of workspace attn_bwd needs (8 * B*H*N), or -1
+ * if the sizes are invalid.  Pure host computation; enqueues nothing.
+ */
+int64_t attn_bwd_workspace(int64_t B, int64_t H, int64_t N);
 
 /*
  * row_softmax - y[r, :] = softmax(x[r, :]) for r < M.

@@ -35,6 +35,12 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
 
 
+def test_every_bound_entry_point_is_declared():
+    """The binding calls nothing the header does not declare, and the header
+    declares nothing the binding leaves out."""
+    assert set(osc.EXPORTS) == declared_functions()
+
+
 def test_status_strings():
     for code in osc.STATUS:
         s = osc.attn_status_str(code)
