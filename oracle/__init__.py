@@ -17,7 +17,9 @@ statement):
 * row softmax: the softmax kernel study (lpnh.cn/news/2830604), section 3.1
   (double-precision stable softmax as the CPU reference);
 * attention backward: the gradients of the attention definition (the FA
-  page, section 7, only says the LSE is kept for the backward pass);
+  page, section 7, only says the LSE is kept for the backward pass); with
+  grouped K/V heads, the sum of those gradients over each group (the chain
+  rule through the KV page's section 3 head mapping);
 * paged decode: "CUDA KV Cache: paged storage and long-context decode"
   (chengzipai.xyz), sections 2 (page-table addressing), 3 (query-head groups
   share a K/V head) and 5 (attention of the new token over the cached ones).
@@ -227,6 +229,37 @@ def attn_rows_gqa(q, k, v, causal: bool, rows, nthreads: int | None = None):
     H = q.shape[1]
     return attn_rows(q, _kv_for_query_heads(k, H), _kv_for_query_heads(v, H), causal, rows,
                      nthreads)
+
+
+def attn_bwd_gqa(q, k, v, dout, causal: bool, kv_heads=None, nthreads: int | None = None):
+    """Gradients of sum(O * dout) for grouped-query attention (attn_fwd_gqa).
+
+    q, dout [B,H,N,D]; k, v [B,Hkv,N,D].  Query head h of batch b reads K/V
+    head kv_head(h) (KV page, section 3), so by the chain rule dQ_h is the
+    plain backward of head h against that K/V head, and dK, dV of a K/V head
+    are the sums over its group of the per-query-head dK, dV.
+
+    kv_heads: flat K/V head ids b*Hkv + j to compute (all if None).  Returns
+    (dq, dk, dv): dq [B,H,N,D] and dk, dv [B,Hkv,N,D] when kv_heads is None;
+    otherwise dq [len(kv_heads)*g, N, D] (the group's query heads in order)
+    and dk, dv [len(kv_heads), N, D].
+    """
+    B, H, N, D = q.shape
+    Hkv = k.shape[1]
+    g = H // Hkv
+    if Hkv < 1 or H % Hkv or k.shape != (B, Hkv, N, D) or v.shape != k.shape:
+        raise ValueError("k, v must be [B, Hkv, N, D] with Hkv dividing H")
+    all_kv = kv_heads is None
+    kv_heads = np.arange(B * Hkv) if all_kv else np.asarray(kv_heads, dtype=np.int64)
+    heads = np.asarray([(f // Hkv) * H + (f % Hkv) * g + i for f in kv_heads for i in range(g)],
+                       dtype=np.int64)
+    dq, dk_h, dv_h = attn_bwd(q, _kv_for_query_heads(k, H), _kv_for_query_heads(v, H), dout,
+                              causal, heads=heads, nthreads=nthreads)
+    dk = dk_h.reshape(len(kv_heads), g, N, D).sum(axis=1)
+    dv = dv_h.reshape(len(kv_heads), g, N, D).sum(axis=1)
+    if all_kv:
+        return dq.reshape(B, H, N, D), dk.reshape(B, Hkv, N, D), dv.reshape(B, Hkv, N, D)
+    return dq, dk, dv
 
 
 def attn_scores(q, k, causal: bool, i: int) -> np.ndarray:

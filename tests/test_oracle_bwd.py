@@ -107,3 +107,80 @@ def test_selected_heads_equal_the_full_result():
     part = oracle.attn_bwd(q, k, v, do, True, heads=[4, 1])
     for f, p in zip(full, part):
         assert np.array_equal(f.reshape(6, 20, 8)[[4, 1]], p)
+
+
+# ------------------------------------------------- grouped K/V heads (GQA)
+
+def autograd_gqa(q, k, v, do, causal):
+    """torch float64 autograd through repeat_interleave of the K/V heads."""
+    qq, kk, vv = [x.clone().requires_grad_() for x in (q, k, v)]
+    g = q.shape[1] // k.shape[1]
+    kr = torch.repeat_interleave(kk, g, dim=1)
+    vr = torch.repeat_interleave(vv, g, dim=1)
+    N, D = q.shape[-2], q.shape[-1]
+    s = qq @ kr.transpose(-1, -2) / np.sqrt(D)
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    o = torch.softmax(s, -1) @ vr
+    (o * do).sum().backward()
+    return qq.grad.numpy(), kk.grad.numpy(), vv.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", [(1, 4, 2, 17, 8), (2, 6, 3, 33, 16), (1, 8, 1, 40, 32)])
+def test_gqa_matches_torch_autograd_float64(shape, causal):
+    B, H, Hkv, N, D = shape
+    q = rand(B, H, N, D, scale=1.5, seed=70)
+    k = rand(B, Hkv, N, D, scale=1.5, seed=71)
+    v = rand(B, Hkv, N, D, seed=72)
+    do = rand(B, H, N, D, seed=73)
+    dq, dk, dv = oracle.attn_bwd_gqa(q, k, v, do, causal)
+    assert dk.shape == (B, Hkv, N, D) and dq.shape == (B, H, N, D)
+    rq, rk, rv = autograd_gqa(q, k, v, do, causal)
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_gqa_with_one_head_per_group_is_the_plain_backward():
+    q, k, v, do = (rand(2, 3, 21, 16, seed=80 + s) for s in range(4))
+    for causal in (True, False):
+        a = oracle.attn_bwd_gqa(q, k, v, do, causal)
+        b = oracle.attn_bwd(q, k, v, do, causal)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+def test_gqa_group_sums_and_invariants():
+    """dK of a shared head is the sum of the group's per-head dK against that
+    head (so its keys still sum to zero); dV of a shared head sums to the sum
+    of the group's dO."""
+    B, H, Hkv, N, D = 1, 6, 2, 25, 8
+    q, do = rand(B, H, N, D, seed=90), rand(B, H, N, D, seed=91)
+    k, v = rand(B, Hkv, N, D, scale=2.0, seed=92), rand(B, Hkv, N, D, seed=93)
+    dq, dk, dv = oracle.attn_bwd_gqa(q, k, v, do, True)
+    g = H // Hkv
+    for j in range(Hkv):
+        acc_k = np.zeros((N, D))
+        acc_v = np.zeros((N, D))
+        for h in range(j * g, (j + 1) * g):
+            dqh, dkh, dvh = oracle.attn_bwd(q[:, h:h + 1], k[:, j:j + 1], v[:, j:j + 1],
+                                            do[:, h:h + 1], True)
+            assert np.array_equal(dqh[0, 0], dq[0, h])
+            acc_k += dkh[0, 0]
+            acc_v += dvh[0, 0]
+        np.testing.assert_allclose(dk[0, j], acc_k, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dv[0, j], acc_v, rtol=0, atol=1e-13)
+        assert np.abs(dk[0, j].sum(axis=0)).max() < 1e-12
+        np.testing.assert_allclose(dv[0, j].sum(axis=0), do[0, j * g:(j + 1) * g].numpy().sum(axis=(0, 1)),
+                                   rtol=0, atol=1e-12)
+
+
+def test_gqa_selected_kv_heads_equal_the_full_result():
+    B, H, Hkv, N, D = 2, 4, 2, 19, 8
+    q, do = rand(B, H, N, D, seed=100), rand(B, H, N, D, seed=101)
+    k, v = rand(B, Hkv, N, D, seed=102), rand(B, Hkv, N, D, seed=103)
+    dq, dk, dv = oracle.attn_bwd_gqa(q, k, v, do, True)
+    pq, pk, pv = oracle.attn_bwd_gqa(q, k, v, do, True, kv_heads=[3, 0])
+    assert np.array_equal(pk, dk.reshape(4, N, D)[[3, 0]])
+    assert np.array_equal(pv, dv.reshape(4, N, D)[[3, 0]])
+    assert np.array_equal(pq, dq.reshape(8, N, D)[[6, 7, 0, 1]])

@@ -156,3 +156,32 @@ def test_gqa_pin_catches_wrong_head_map(monkeypatch):
     assert gqa_sdpa_check(q, k, v, True) <= 1e-12
     monkeypatch.setattr(oracle, "kv_head", lambda h, H, Hkv: h % Hkv)
     assert gqa_sdpa_check(q, k, v, True) > 1e-3
+
+
+def test_gqa_backward_pins_catch_wrong_head_map_and_missing_group_sum(monkeypatch):
+    """Planted in the oracle's Python layer: (a) h % Hkv in place of h // g for
+    the K/V head of a query head; (b) dK, dV of a shared head taken from the
+    first query head of its group instead of summed over the group.  The
+    autograd pin rejects both."""
+    import numpy as np
+    kw = {"shape": (1, 4, 2, 17, 8), "causal": True}
+    bpins.test_gqa_matches_torch_autograd_float64(**kw)
+    with monkeypatch.context() as m:
+        m.setattr(oracle, "kv_head", lambda h, H, Hkv: h % Hkv)
+        with pytest.raises(AssertionError):
+            bpins.test_gqa_matches_torch_autograd_float64(**kw)
+    real = oracle.attn_bwd_gqa
+
+    def first_head_only(q, k, v, dout, causal, kv_heads=None, nthreads=None):
+        B, H, N, D = q.shape
+        Hkv = k.shape[1]
+        dq, dk_h, dv_h = oracle.attn_bwd(q, oracle._kv_for_query_heads(k, H),
+                                         oracle._kv_for_query_heads(v, H), dout, causal)
+        g = H // Hkv
+        return (dq, np.ascontiguousarray(dk_h[:, ::g]), np.ascontiguousarray(dv_h[:, ::g]))
+
+    with monkeypatch.context() as m:
+        m.setattr(oracle, "attn_bwd_gqa", first_head_only)
+        with pytest.raises(AssertionError):
+            bpins.test_gqa_matches_torch_autograd_float64(**kw)
+    assert oracle.attn_bwd_gqa is real
