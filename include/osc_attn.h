@@ -18,6 +18,7 @@
  *                whose partial states are merged afterwards.
  *   paged_decode one decode step over a paged K/V cache.
  *   attn_bwd     gradients of attn_fwd with respect to q, k and v.
+ *   attn_bwd_gqa the same for attn_fwd_gqa (grouped K/V heads).
  *
  *   row_softmax  y = softmax(x) along each row of an FP32 matrix, computed
  *                with the online (m, d) recurrence and two-level merge of the
@@ -267,8 +268,34 @@ attn_status_t attn_bwd(const void *q, const void *k, const void *v, const float 
                        void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /*
- * attn_bwd_workspace - bytes of workspace attn_bwd needs (8 * B*H*N), or -1
- * if the sizes are invalid.  Pure host computation; enqueues nothing.
+ * attn_bwd_gqa - attn_bwd for attn_fwd_gqa: Hkv key/value heads shared by
+ * groups of g = H / Hkv query heads.
+ *
+ * Query head h of batch b reads K/V head floor(h / g) of the same batch
+ * ("CUDA KV Cache: paged storage and long-context decode" (chengzipai.xyz),
+ * section 3), so by the chain rule dQ of head h is the attn_bwd formula
+ * against that K/V head, and dK, dV of a K/V head are the sums over its
+ * group of the formula's per-head dK, dV.  The sum is accumulated inside one
+ * workgroup per key tile (no atomics; bit-for-bit repeatable).
+ *
+ *   q, o, dout, dq  [B, H, N, D];  lse [B, H, N]  (as for attn_bwd).
+ *   k, v     [B, Hkv, N, D] of `dtype`, 16-byte aligned: attn_fwd_gqa's K, V.
+ *   dk, dv   [B, Hkv, N, D] FP32 outputs, 16-byte aligned.
+ *   Hkv      1 <= Hkv <= H and H % Hkv == 0, else ATTN_ERR_SHAPE.
+ *   workspace  at least attn_bwd_workspace(B, H, N) bytes (per query row).
+ * Everything else (D, dtype, causal, limits, errors, stream) is as for
+ * attn_bwd; attn_bwd is this call with Hkv = H.
+ */
+attn_status_t attn_bwd_gqa(const void *q, const void *k, const void *v, const float *o,
+                           const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                           int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal,
+                           attn_dtype_t dtype, void *workspace, int64_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * attn_bwd_workspace - bytes of workspace attn_bwd and attn_bwd_gqa need
+ * (8 * B*H*N, H the query heads), or -1 if the sizes are invalid.  Pure host
+ * computation; enqueues nothing.
  */
 int64_t attn_bwd_workspace(int64_t B, int64_t H, int64_t N);
 

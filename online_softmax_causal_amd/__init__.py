@@ -19,6 +19,8 @@ The entry points mirror the C ABI in ``include/osc_attn.h``:
     paged_decode_workspace(B, Hq, Hkv, D, page_size, max_pages, num_splits=0)
     attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, dtype, workspace,
              workspace_bytes, stream=None)
+    attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, causal, dtype,
+                 workspace, workspace_bytes, stream=None)
     attn_bwd_workspace(B, H, N)
     attn_status_str(status)
 
@@ -49,7 +51,7 @@ STATUS = {
     7: "ATTN_ERR_WORKSPACE",
 }
 EXPORTS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace",
-           "paged_decode", "paged_decode_workspace", "attn_bwd", "attn_bwd_workspace",
+           "paged_decode", "paged_decode_workspace", "attn_bwd", "attn_bwd_gqa", "attn_bwd_workspace",
            "row_softmax", "attn_status_str")
 
 _lib = None
@@ -90,6 +92,9 @@ def load():
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                              ctypes.c_int, vp, i64, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                 ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    lib.attn_bwd_gqa.restype = ctypes.c_int
     lib.attn_bwd_workspace.argtypes = [i64, i64, i64]
     lib.attn_bwd_workspace.restype = i64
     lib.row_softmax.argtypes = [vp, vp, i64, i64, vp]
@@ -199,6 +204,17 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, dtype, works
                          _dtype(dtype), _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != 0:
         raise AttnError(st, "attn_bwd")
+
+
+def attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, causal, dtype, workspace,
+                 workspace_bytes, stream=None) -> None:
+    """Enqueue attention backward with Hkv shared K/V heads (k, v, dk, dv [B, Hkv, N, D])."""
+    st = load().attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                             _ptr(dk), _ptr(dv), int(B), int(H), int(Hkv), int(N), int(D),
+                             int(bool(causal)), _dtype(dtype), _ptr(workspace),
+                             int(workspace_bytes), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_gqa")
 
 
 def row_softmax(x, y, M, N, stream=None) -> None:

@@ -86,21 +86,30 @@ int64_t attn_bwd_workspace(int64_t B, int64_t H, int64_t N) {
     return 8 * rows;
 }
 
+attn_status_t attn_bwd_gqa(const void* q, const void* k, const void* v, const float* o,
+                           const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                           int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t D, int causal,
+                           attn_dtype_t dtype, void* workspace, int64_t workspace_bytes,
+                           hipStream_t stream) {
+    // validate_attn checks q, k, v and the FP32 pair (o, lse) as inputs here.
+    attn_status_t st = osc::validate_attn(q, k, v, o, lse, B, H, Hkv, N, D, dtype);
+    if (st != ATTN_OK) return st;
+    st = osc::validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H,
+                           Hkv, N, D);
+    if (st != ATTN_OK) return st;
+    const hipError_t e = osc::launch_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv,
+                                              static_cast<float*>(workspace), (int)B, (int)H,
+                                              (int)Hkv, (int)N, (int)D, causal != 0,
+                                              dtype == ATTN_BF16, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 attn_status_t attn_bwd(const void* q, const void* k, const void* v, const float* o,
                        const float* lse, const void* dout, float* dq, float* dk, float* dv,
                        int64_t B, int64_t H, int64_t N, int64_t D, int causal, attn_dtype_t dtype,
                        void* workspace, int64_t workspace_bytes, hipStream_t stream) {
-    // validate_attn checks q, k, v and the FP32 pair (o, lse) as inputs here.
-    attn_status_t st = osc::validate_attn(q, k, v, o, lse, B, H, H, N, D, dtype);
-    if (st != ATTN_OK) return st;
-    st = osc::validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N,
-                           D);
-    if (st != ATTN_OK) return st;
-    const hipError_t e = osc::launch_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv,
-                                              static_cast<float*>(workspace), (int)B, (int)H,
-                                              (int)N, (int)D, causal != 0, dtype == ATTN_BF16,
-                                              stream);
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    return attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, D, causal, dtype, workspace,
+                        workspace_bytes, stream);
 }
 
 // Decode split plan and workspace size for valid sizes; false if they are not.

@@ -64,7 +64,10 @@ struct BwdArgs {
     float* dv;
     float* dd;          // workspace [B, H, N]: D_i
     float* lse2;        // workspace [B, H, N]: lse_i * log2(e)
-    int BH;
+    int BH;             // B * H (query heads)
+    int H;              // query heads per batch
+    int Hkv;            // key/value heads per batch (divides H)
+    int BHkv;           // B * Hkv
     int N;
     float scale_log2;   // log2(e) / sqrt(D)
     float scale;        // 1 / sqrt(D)
@@ -227,9 +230,14 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     const int col = lane & 31, g = lane >> 5;
     const int N = a.N;
     const int nkt = (N + kDkdvRows - 1) / kDkdvRows;
-    int kt, bh;
-    bwd_work(blockIdx.x, a.BH, nkt, false, &kt, &bh);
-    const int64_t head = (int64_t)bh * N;
+    // Workgroup: one key tile of one K/V head.  Its dK and dV sum over the
+    // g query heads of the group (KV page, section 3: query head h reads K/V
+    // head floor(h / g)), whose Q / dO tiles stream through one sequence.
+    int kt, bkv;
+    bwd_work(blockIdx.x, a.BHkv, nkt, false, &kt, &bkv);
+    const int64_t head = (int64_t)bkv * N;   // K/V / dK / dV rows of this head
+    const int grp = a.H / a.Hkv;
+    const int hq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * grp;  // first query head
     const int kw = kt * kDkdvRows + 32 * w;  // first key of this wave
     const int key = kw + col;
 
@@ -261,24 +269,29 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     // first key contribute.
     const int nqt = (N + kBwdTile - 1) / kBwdTile;
     const int qt0 = CAUSAL ? (kt * kDkdvRows) / kBwdTile : 0;
-    auto stage = [&](int it) { return lds + (it % kBwdStages) * STAGE; };
+    // Streamed tiles, numbered fi = i * nt + (it - qt0) for query head
+    // hq0 + i of the group and query tile it.
+    const int nt = nqt - qt0;
+    const int nflat = grp * nt;
+    auto stage = [&](int fi) { return lds + (fi % kBwdStages) * STAGE; };
     // Waves 0 and 1 also copy the tile's lse2 and D rows (one 4-byte copy each).
-    auto issue = [&](int it) {
-        if (it >= nqt) return;
-        u16* st = stage(it);
-        const int r0 = it * kBwdTile;
-        copy_tile<D, kDkdvWaves>(a.q + head * D, st, r0, N, w, lane);
-        copy_tile<D, kDkdvWaves>(a.dout + head * D, st + TILE, r0, N, w, lane);
+    auto issue = [&](int fi) {
+        if (fi >= nflat) return;
+        u16* st = stage(fi);
+        const int64_t qhead = (int64_t)(hq0 + fi / nt) * N;
+        const int r0 = (qt0 + fi % nt) * kBwdTile;
+        copy_tile<D, kDkdvWaves>(a.q + qhead * D, st, r0, N, w, lane);
+        copy_tile<D, kDkdvWaves>(a.dout + qhead * D, st + TILE, r0, N, w, lane);
         if (w < 2) {
             const int row = min(r0 + lane, N - 1);
-            const float* src = w == 0 ? a.lse2 + head : a.dd + head;
+            const float* src = w == 0 ? a.lse2 + qhead : a.dd + qhead;
             copy_to_lds4(src, (unsigned)(row * 4), st + 2 * TILE + w * 2 * kBwdTile);
         }
     };
-    // Tile it+1 complete for this wave (tile it+2 may stay in flight), then
+    // Tile fi+1 complete for this wave (tile fi+2 may stay in flight), then
     // for all waves.
-    auto wait_next = [&](int it) {
-        if (it + 2 < nqt) {
+    auto wait_next = [&](int fi) {
+        if (fi + 2 < nflat) {
             if (w < 2)
                 wait_vmcnt<2 * LPM + 1>();
             else
@@ -341,9 +354,9 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     std::integral_constant<bool, false> plain;
     std::integral_constant<bool, true> masked;
 
-    issue(qt0);
-    issue(qt0 + 1);
-    if (qt0 + 1 < nqt) {
+    issue(0);
+    issue(1);
+    if (1 < nflat) {
         if (w < 2)
             wait_vmcnt<2 * LPM + 1>();
         else
@@ -353,9 +366,10 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    for (int it = qt0; it < nqt; ++it) {
-        issue(it + 2);
-        const u16* st = stage(it);
+    for (int fi = 0; fi < nflat; ++fi) {
+        issue(fi + 2);
+        const int it = qt0 + fi % nt;
+        const u16* st = stage(fi);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int qb = it * kBwdTile + 32 * b;  // first query row of the block
@@ -365,7 +379,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
             else
                 block(st, b, qb, plain);
         }
-        wait_next(it);
+        wait_next(fi);
     }
 
     // Lane (col, g) holds d = 32 mt + 8 (i / 4) + 4 g + i % 4 of key `key`.
@@ -405,6 +419,8 @@ attn_bwd_dq_kernel(BwdArgs a) {
     int t, bh;
     bwd_work(blockIdx.x, a.BH, nq, CAUSAL, &t, &bh);
     const int64_t head = (int64_t)bh * N;
+    // K/V head of this query head (KV page, section 3).
+    const int64_t kvhead = (int64_t)((bh / a.H) * a.Hkv + (bh % a.H) / (a.H / a.Hkv)) * N;
     const int row0 = t * kDqRows + 32 * w;  // first query row of this wave
     const int row = row0 + col;
 
@@ -438,8 +454,8 @@ attn_bwd_dq_kernel(BwdArgs a) {
     auto issue = [&](int it) {
         if (it >= ntiles) return;
         u16* st = stage(it);
-        copy_tile<D, kDqWaves>(a.k + head * D, st, it * kBwdTile, N, w, lane);
-        copy_tile<D, kDqWaves>(a.v + head * D, st + TILE, it * kBwdTile, N, w, lane);
+        copy_tile<D, kDqWaves>(a.k + kvhead * D, st, it * kBwdTile, N, w, lane);
+        copy_tile<D, kDqWaves>(a.v + kvhead * D, st + TILE, it * kBwdTile, N, w, lane);
     };
     auto finish = [&](int it) {
         if (it + 2 < ntiles)
@@ -535,7 +551,7 @@ hipError_t launch_bwd(BwdArgs a, hipStream_t stream) {
                                    dim3(pre_grid), dim3(256), params, 0, stream);
     if (e != hipSuccess) return e;
     constexpr int kv_rows = 32 * dkdv_waves<D>();
-    const unsigned grid = (unsigned)(((a.N + kv_rows - 1) / kv_rows) * a.BH);
+    const unsigned grid = (unsigned)(((a.N + kv_rows - 1) / kv_rows) * a.BHkv);
     e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<BF16, D, CAUSAL>),
                         dim3(grid), dim3(64 * dkdv_waves<D>()), params, 0, stream);
     if (e != hipSuccess) return e;
@@ -548,8 +564,8 @@ hipError_t launch_bwd(BwdArgs a, hipStream_t stream) {
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const float* o,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                           float* workspace, int B, int H, int N, int D, bool causal, bool bf16,
-                           hipStream_t stream) {
+                           float* workspace, int B, int H, int Hkv, int N, int D, bool causal,
+                           bool bf16, hipStream_t stream) {
     BwdArgs a{};
     a.q = static_cast<const u16*>(q);
     a.k = static_cast<const u16*>(k);
@@ -561,6 +577,9 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const fl
     a.dk = dk;
     a.dv = dv;
     a.BH = B * H;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.BHkv = B * Hkv;
     a.N = N;
     a.dd = workspace;
     a.lse2 = workspace + (int64_t)B * H * N;

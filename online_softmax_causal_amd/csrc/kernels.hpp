@@ -41,11 +41,11 @@ hipError_t launch_splitkv_merge(const float* part_o, const float2* part_ml, floa
                                 hipStream_t stream);
 
 // Attention backward: D_i and lse_i log2(e) into workspace [2, B*H*N] (FP32),
-// then the dK/dV and dQ kernels.
+// then the dK/dV and dQ kernels.  K, V, dK, dV have Hkv heads (Hkv divides H).
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const float* o,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                           float* workspace, int B, int H, int N, int D, bool causal, bool bf16,
-                           hipStream_t stream);
+                           float* workspace, int B, int H, int Hkv, int N, int D, bool causal,
+                           bool bf16, hipStream_t stream);
 
 // Paged decode: tokens per tile, and the most tokens one segment may hold
 // (its page ids are staged in LDS, one slot per page).

@@ -78,17 +78,19 @@ inline attn_status_t validate_workspace(const void* ws, int64_t ws_bytes, int64_
 inline attn_status_t validate_bwd(const void* q, const void* k, const void* v, const float* o,
                                   const float* lse, const void* dout, const float* dq,
                                   const float* dk, const float* dv, const void* ws,
-                                  int64_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t D) {
+                                  int64_t ws_bytes, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                                  int64_t D) {
     if (!dout || !dq || !dk || !dv || !ws) return ATTN_ERR_NULL;
     if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
         !aligned(ws, 16))
         return ATTN_ERR_ALIGN;
-    const int64_t total = B * H * N * D, rows = B * H * N;
+    // Sizes were checked by validate_attn (below 2^62, Hkv divides H).
+    const int64_t total = B * H * N * D, rows = B * H * N, kv = B * Hkv * N * D;
     if (ws_bytes < 8 * rows) return ATTN_ERR_WORKSPACE;
     const void* ins[6] = {q, k, v, o, lse, dout};
-    const int64_t in_bytes[6] = {total * 2, total * 2, total * 2, total * 4, rows * 4, total * 2};
+    const int64_t in_bytes[6] = {total * 2, kv * 2, kv * 2, total * 4, rows * 4, total * 2};
     const void* outs[4] = {dq, dk, dv, ws};
-    const int64_t out_bytes[4] = {total * 4, total * 4, total * 4, rows * 8};
+    const int64_t out_bytes[4] = {total * 4, kv * 4, kv * 4, rows * 8};
     for (int i = 0; i < 4; ++i) {
         for (int j = 0; j < 6; ++j)
             if (overlap(outs[i], out_bytes[i], ins[j], in_bytes[j])) return ATTN_ERR_ALIAS;

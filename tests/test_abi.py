@@ -225,6 +225,38 @@ def test_attn_bwd_workspace_and_rejections():
     assert call_bwd(ws=BASE + 192 * MB) == 6             # workspace on O
 
 
+def call_bwd_gqa(q=BASE, k=BASE + 64 * MB, v=BASE + 128 * MB, o=BASE + 192 * MB,
+                 lse=BASE + 320 * MB, do=BASE + 400 * MB, dq=BASE + 500 * MB, dk=BASE + 700 * MB,
+                 dv=BASE + 900 * MB, B=1, H=8, Hkv=2, N=4096, D=128, causal=1, dtype=0,
+                 ws=BASE + 1100 * MB, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = max(osc.attn_bwd_workspace(B, H, N), 0)
+    return osc.load().attn_bwd_gqa(q, k, v, o, lse, do, dq, dk, dv, B, H, Hkv, N, D, causal,
+                                   dtype, ws, ws_bytes, None)
+
+
+def test_attn_bwd_gqa_rejections():
+    # Sizes at B1 H8 Hkv2 N4096 D128: q/dO 8 MiB, k/v 2 MiB, dQ 16 MiB, dK/dV 4 MiB.
+    assert call_bwd_gqa(k=None) == 1
+    assert call_bwd_gqa(Hkv=3) == 2                       # does not divide H
+    assert call_bwd_gqa(Hkv=16) == 2                      # more K/V heads than query heads
+    assert call_bwd_gqa(Hkv=0) == 2
+    assert call_bwd_gqa(dk=BASE + 700 * MB + 4) == 4
+    assert call_bwd_gqa(ws_bytes=8 * 8 * 4096 - 4) == 7   # workspace follows the query heads
+    assert call_bwd_gqa(dk=BASE + 64 * MB + 2 * MB - 4096) == 6   # dK overlaps the end of K
+    assert call_bwd_gqa(dv=BASE + 700 * MB + 4 * MB - 256) == 6   # dV overlaps the end of dK
+
+
+def test_attn_bwd_is_the_gqa_call_with_one_head_per_group():
+    """attn_bwd rejects exactly what attn_bwd_gqa with Hkv = H rejects (every
+    case here is invalid, so nothing is launched)."""
+    for kw in ({"do": None}, {"N": 0}, {"D": 96}, {"dq": BASE + 500 * MB + 8},
+               {"dk": BASE + 64 * MB}, {"ws_bytes": 8 * 2 * 4096 - 4}):
+        ref = call_bwd(**kw)
+        assert ref != 0
+        assert call_bwd_gqa(H=2, Hkv=2, **kw) == ref, kw
+
+
 def call_softmax(x=BASE, y=BASE + 64 * MB, M=4, N=100):
     return osc.load().row_softmax(x, y, M, N, None)
 

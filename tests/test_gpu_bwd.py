@@ -90,3 +90,79 @@ def test_headline_shape_sampled_heads():
     heads = [0, w.H - 1]
     ref = oracle.attn_bwd(q, k, v, do, w.causal, heads=heads)
     check("bwd C4 heads %s" % heads, [g.reshape(-1, w.N, w.D)[heads] for g in got], ref, w.dtype)
+
+
+# ------------------------------------------------- grouped K/V heads (GQA)
+
+def run_bwd_gqa(q, k, v, do, causal, dtype):
+    d = dev()
+    B, H, N, D = q.shape
+    Hkv = k.shape[1]
+    qd, kd, vd, dod = (t.to(d) for t in (q, k, v, do))
+    o = torch.empty((B, H, N, D), dtype=torch.float32, device=d)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=d)
+    osc.attn_fwd_gqa(qd, kd, vd, o, lse, B, H, Hkv, N, D, causal, dtype)
+    dq = torch.full((B, H, N, D), float("nan"), dtype=torch.float32, device=d)
+    dk = torch.full((B, Hkv, N, D), float("nan"), dtype=torch.float32, device=d)
+    dv = torch.full((B, Hkv, N, D), float("nan"), dtype=torch.float32, device=d)
+    need = osc.attn_bwd_workspace(B, H, N)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=d)
+    osc.attn_bwd_gqa(qd, kd, vd, o, lse, dod, dq, dk, dv, B, H, Hkv, N, D, causal, dtype, ws, need)
+    torch.cuda.synchronize()
+    return [g.cpu().double().numpy() for g in (dq, dk, dv)]
+
+
+GQA_SMALL = [
+    # (B, H, Hkv, N, D): groups of 2, 3, 4 and 8 (MQA), one row, ragged lengths
+    (1, 4, 2, 65, 128), (2, 6, 2, 129, 64), (1, 8, 1, 200, 128), (1, 8, 2, 1, 128),
+    (2, 4, 1, 333, 64), (1, 6, 3, 97, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", GQA_SMALL, ids=lambda s: "B%dH%dHkv%dN%dD%d" % s)
+def test_gqa_small_shapes_match_oracle(shape, causal, dtype):
+    B, H, Hkv, N, D = shape
+    seed = 9200 + 7 * N + D + Hkv + (1 if causal else 0)
+    q, k, v, do = workloads.bwd_gqa_inputs(B, H, Hkv, N, D, dtype, seed, sigma_qk=1.5)
+    name = "bwd gqa %s %s B%d H%d Hkv%d N%d D%d seed %d" % (
+        "causal" if causal else "full", dtype, B, H, Hkv, N, D, seed)
+    print("running", name, flush=True)
+    got = run_bwd_gqa(q, k, v, do, causal, dtype)
+    check(name, got, oracle.attn_bwd_gqa(q, k, v, do, causal), dtype)
+
+
+def test_gqa_with_one_head_per_group_equals_attn_bwd():
+    q, k, v, do = workloads.bwd_inputs(1, 3, 200, 128, "bf16", 9201)
+    print("running bwd gqa Hkv = H", flush=True)
+    a = run_bwd_gqa(q, k, v, do, True, "bf16")
+    b = run_bwd(q, k, v, do, True, "bf16")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_gqa_deterministic():
+    q, k, v, do = workloads.bwd_gqa_inputs(1, 8, 2, 500, 128, "f16", 9202)
+    print("running bwd gqa determinism", flush=True)
+    a = run_bwd_gqa(q, k, v, do, True, "f16")
+    b = run_bwd_gqa(q, k, v, do, True, "f16")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_gqa_benchmark_shape_sampled():
+    """Causal fp16 B1 H32 Hkv8 N8192 D128 (the G1 shape): dK, dV of one K/V
+    head and dQ of its four query heads against the oracle, finiteness of all."""
+    w = workloads.GQA["G1"]
+    q, k, v, do = workloads.bwd_gqa_inputs(w.B, w.H, w.Hkv, w.N, w.D, w.dtype, w.seed)
+    print("running bwd gqa", w.describe(), flush=True)
+    got = run_bwd_gqa(q, k, v, do, w.causal, w.dtype)
+    for x in got:
+        assert np.isfinite(x).all()
+    j = w.Hkv - 1
+    g = w.H // w.Hkv
+    rq, rk, rv = oracle.attn_bwd_gqa(q, k, v, do, w.causal, kv_heads=[j])
+    check("bwd G1 kv head %d" % j,
+          [got[0].reshape(-1, w.N, w.D)[j * g:(j + 1) * g], got[1].reshape(-1, w.N, w.D)[[j]],
+           got[2].reshape(-1, w.N, w.D)[[j]]], [rq, rk, rv], w.dtype)

@@ -187,6 +187,19 @@ def bwd_inputs(B: int, H: int, N: int, D: int, dtype: str, seed: int, sigma_qk: 
     return q.contiguous(), k.contiguous(), v.contiguous(), do.contiguous()
 
 
+def bwd_gqa_inputs(B: int, H: int, Hkv: int, N: int, D: int, dtype: str, seed: int,
+                   sigma_qk: float = 1.0, sigma_v: float = 1.0, sigma_do: float = 1.0):
+    """q [B,H,N,D], k, v [B,Hkv,N,D], dO [B,H,N,D]; drawn in that order."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    td = TORCH_DTYPE[dtype]
+    q = (torch.randn((B, H, N, D), generator=g, dtype=torch.float32) * sigma_qk).to(td)
+    k = (torch.randn((B, Hkv, N, D), generator=g, dtype=torch.float32) * sigma_qk).to(td)
+    v = (torch.randn((B, Hkv, N, D), generator=g, dtype=torch.float32) * sigma_v).to(td)
+    do = (torch.randn((B, H, N, D), generator=g, dtype=torch.float32) * sigma_do).to(td)
+    return q.contiguous(), k.contiguous(), v.contiguous(), do.contiguous()
+
+
 def workload_inputs(w: AttnWorkload):
     if w.Hkv is not None:
         return gqa_inputs(w.B, w.H, w.Hkv, w.N, w.D, w.dtype, w.seed, w.sigma_qk, w.sigma_v)
