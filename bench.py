@@ -161,6 +161,26 @@ def extra_configs(dev):
                               "ms": round(med, 5), "ms_min": round(mn, 5), "tflops": round(tf, 2),
                               "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
         del q, k, v, do, o, lse, dq, dk, dv, ws
+    # Backward with grouped K/V heads (G1): same algorithmic FLOP as the
+    # per-query-head backward (dK, dV of a shared head sum over its group).
+    w = workloads.GQA["G1"]
+    q, k, v, do = (t.to(dev) for t in workloads.bwd_gqa_inputs(w.B, w.H, w.Hkv, w.N, w.D, w.dtype,
+                                                               w.seed))
+    o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    osc.attn_fwd_gqa(q, k, v, o, lse, w.B, w.H, w.Hkv, w.N, w.D, w.causal, w.dtype)
+    dq = torch.empty_like(o)
+    dk, dv = (torch.empty((w.B, w.Hkv, w.N, w.D), dtype=torch.float32, device=dev) for _ in range(2))
+    need = osc.attn_bwd_workspace(w.B, w.H, w.N)
+    ws = torch.empty((need // 4,), dtype=torch.float32, device=dev)
+    fn = lambda: osc.attn_bwd_gqa(q, k, v, o, lse, do, dq, dk, dv, w.B, w.H, w.Hkv, w.N, w.D,
+                                  w.causal, w.dtype, ws, need)
+    med, mn = time_groups(fn, stream)
+    tf = 2.5 * w.flops / (med * 1e-3) / 1e12
+    out["G1 bwd"] = {"workload": w.describe().replace("fwd", "bwd"), "entry": "attn_bwd_gqa",
+                     "ms": round(med, 5), "ms_min": round(mn, 5), "tflops": round(tf, 2),
+                     "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+    del q, k, v, do, o, lse, dq, dk, dv, ws
     # Paged grouped-query decode (KV page, section 8 shapes), automatic split;
     # attention kernel and merge inside the timed region.  HBM-bound: GB/s of
     # algorithmic bytes (K and V of every cached token once, q, o, lse).

@@ -9,15 +9,19 @@
 // gradients are those of the definition:
 //     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_d dO_id O_id,
 //     dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D)
-// (D_i = sum_j P_ij dP_ij because O_i = sum_j P_ij v_j).
+// (D_i = sum_j P_ij dP_ij because O_i = sum_j P_ij v_j).  With grouped K/V
+// heads (query head h reads K/V head floor(h / g), "CUDA KV Cache: paged
+// storage and long-context decode" (chengzipai.xyz), section 3), dK and dV of
+// a K/V head are the sums of these over the g query heads of its group.
 //
 // Three kernels, all on one stream:
 //   attn_bwd_pre_kernel   D_i and the base-2 log-sum-exp lse_i * log2(e) of
 //                         every row, into the caller's workspace (HBM-bound);
 //   attn_bwd_dkdv_kernel  key-major: a workgroup keeps 32 keys per wave (4
-//                         waves at D = 128, 8 at D = 64) of K and V in
-//                         registers and streams 64-row tiles of
-//                         Q and dO (with D and lse of those rows) through LDS;
+//                         waves at D = 128, 8 at D = 64) of one K/V head in
+//                         registers and streams 64-row tiles of Q and dO
+//                         (with D and lse of those rows) of every query head
+//                         of the group through LDS;
 //                         dV^T += dO^T P and dK^T += Q^T dS on the MFMA;
 //   attn_bwd_dq_kernel    query-major, like the forward kernel: a workgroup of
 //                         8 waves (two per SIMD) keeps 256 query rows of Q and
