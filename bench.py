@@ -422,6 +422,39 @@ def summarize_sq(dirs, out_path, cmds):
     print("\n".join(lines))
 
 
+def summarize_sq_bwd(dirs, out_path, cmds):
+    """Write profiles/attn_bwd_C4_sq_counters.txt from rocprofv3 --pmc SQ passes of --profile-bwd."""
+    import re
+    import statistics
+    vals = {}
+    for d in dirs:
+        for r in _pmc_rows(d):
+            m = re.search(r"::(attn_bwd_\w+?)<", r["Kernel_Name"])
+            if m:
+                vals.setdefault((m.group(1), r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    lines = ["attention backward kernels, causal fp16 B1 H32 N8192 D128: SQ counters per dispatch "
+             "(rocprofv3 --pmc)", "", "commands (from the repository root, TMPDIR=/tmp):"]
+    lines += ["  " + c for c in cmds]
+    simds, xcds = 256 * 4, 8
+    for kernel in sorted({k for k, _ in vals}):
+        med = {c: statistics.median(v) for (k, c), v in vals.items() if k == kernel}
+        lines += ["", "%s: counter | median over %d dispatches" % (
+            kernel, len(next(v for (k, _), v in vals.items() if k == kernel)))]
+        for c in sorted(med):
+            lines.append("  %s | %.5g" % (c, med[c]))
+        if "GRBM_GUI_ACTIVE" in med and "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            cycles = med["GRBM_GUI_ACTIVE"] / xcds
+            lines.append("  MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x %.4g cycles) = %.3f"
+                         % (cycles, med["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cycles)))
+        if med.get("SQ_INSTS_MFMA"):
+            lines.append("  VALU instructions per MFMA = %.2f" % (med["SQ_INSTS_VALU"] / med["SQ_INSTS_MFMA"]))
+    lines.append("sources_sha256_16: bwd.hip %s" % kernel_source_hash(("bwd.hip",)))
+    lines.append("")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def summarize_trace(trace_dir, out_path, cmd, last):
     """Write a kernel-duration summary from a rocprofv3 --kernel-trace --stats csv run.
 
@@ -455,9 +488,9 @@ def summarize_trace(trace_dir, out_path, cmd, last):
             lines.append("%s: mean of the last %d launches (the timed steps) %.2f us" % (
                 name[:110], len(tail), sum(tail) / len(tail) / 1e3))
     lines.append("sources_sha256_16: attn_fwd.hip+mfma_tile.hpp+online_merge.hpp %s, "
-                 "decode.hip %s, splitkv.hip %s" % (kernel_source_hash(),
-                                                   kernel_source_hash(("decode.hip",)),
-                                                   kernel_source_hash(("splitkv.hip",))))
+                 "decode.hip %s, splitkv.hip %s, bwd.hip %s" % (
+                     kernel_source_hash(), kernel_source_hash(("decode.hip",)),
+                     kernel_source_hash(("splitkv.hip",)), kernel_source_hash(("bwd.hip",))))
     lines.append("")
     with open(out_path, "w") as f:
         f.write("\n".join(lines))
@@ -480,6 +513,7 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
     ap.add_argument("--summarize-sq", nargs="+", metavar="DIR")
+    ap.add_argument("--summarize-sq-bwd", nargs="+", metavar="DIR")
     ap.add_argument("--trace-last", type=int, default=20)
     ap.add_argument("--cmd", default="")
     ap.add_argument("--cmd-fetch", default="")
@@ -488,6 +522,11 @@ def main():
     if args.summarize_sq:
         summarize_sq(args.summarize_sq, os.path.join(ROOT, "profiles", "attn_fwd_C4_sq_counters.txt"),
                      args.cmd.split(" ;; "))
+        return
+    if args.summarize_sq_bwd:
+        summarize_sq_bwd(args.summarize_sq_bwd,
+                         os.path.join(ROOT, "profiles", "attn_bwd_C4_sq_counters.txt"),
+                         args.cmd.split(" ;; "))
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.cmd, args.trace_last)
