@@ -338,12 +338,17 @@ def _per_dispatch(rows, counter, match):
     return [vals[k] for k in sorted(vals, key=lambda x: int(x))]
 
 
+def is_fwd_kernel(name: str) -> bool:
+    """The attention forward kernels (8-wave unit kernel, 4-wave ring kernel)."""
+    return "attn_fwd_units_kernel" in name or "attn_fwd_kernel" in name
+
+
 def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
     """Write profiles/attn_fwd_C4_traffic.txt from two rocprofv3 --pmc runs of --profile-pass."""
     import workloads
     w = workloads.ATTN["C4"]
-    is_attn = lambda n: "attn_fwd_kernel" in n
-    is_copy = lambda n: "attn_fwd_kernel" not in n
+    is_attn = is_fwd_kernel
+    is_copy = lambda n: not is_fwd_kernel(n)
     fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     a_fetch = _per_dispatch(fr, "FETCH_SIZE", is_attn)
     c_fetch = _per_dispatch(fr, "FETCH_SIZE", is_copy)
@@ -358,7 +363,7 @@ def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
     a_written = mean(a_write) * 1024.0 * w_scale
     compulsory = 3 * w.B * w.H * w.N * w.D * 2 + w.B * w.H * w.N * (w.D + 1) * 4
     text = "\n".join([
-        "attn_fwd_kernel, causal fp16 B1 H32 N8192 D128: HBM traffic per launch (rocprofv3 --pmc)",
+        "attn_fwd_units_kernel, causal fp16 B1 H32 N8192 D128: HBM traffic per launch (rocprofv3 --pmc)",
         "",
         "commands (from the repository root, TMPDIR=/tmp):",
         "  " + cmd_fetch,
@@ -392,11 +397,11 @@ def summarize_sq(dirs, out_path, cmds):
     for d in dirs:
         rows = _pmc_rows(d)
         for r in rows:
-            if "attn_fwd_kernel" in r["Kernel_Name"]:
+            if is_fwd_kernel(r["Kernel_Name"]):
                 vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     med = {k: statistics.median(v) for k, v in vals.items()}
     simds, xcds = 256 * 4, 8
-    lines = ["attn_fwd_kernel, causal fp16 B1 H32 N8192 D128: SQ counters per dispatch (rocprofv3 --pmc)",
+    lines = ["attn_fwd_units_kernel, causal fp16 B1 H32 N8192 D128: SQ counters per dispatch (rocprofv3 --pmc)",
              "", "commands (from the repository root, TMPDIR=/tmp):"]
     lines += ["  " + c for c in cmds]
     lines += ["", "counter | per dispatch (3 dispatches) | median"]
@@ -481,8 +486,8 @@ def summarize_trace(trace_dir, out_path, cmd, last):
                 (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     lines.append("")
     for name, d in durs.items():
-        if any(k in name for k in ("attn_fwd_kernel", "softmax", "paged_decode", "splitkv_merge",
-                                   "attn_bwd")):
+        if is_fwd_kernel(name) or any(k in name for k in ("softmax", "paged_decode", "splitkv_merge",
+                                                          "attn_bwd")):
             d.sort()
             tail = [x[1] for x in d[-last:]]
             lines.append("%s: mean of the last %d launches (the timed steps) %.2f us" % (
@@ -604,7 +609,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
-                     "kernel": "attn_fwd_kernel<f16, D=128, causal>",
+                     "kernel": "attn_fwd_units_kernel<f16, D=128, causal>",
                      "kernel_source_sha256_16": kernel_source_hash()},
     }
     if not args.no_cpu:

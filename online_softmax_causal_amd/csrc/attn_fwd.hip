@@ -15,15 +15,16 @@
 // tiles wholly above the diagonal are skipped and only diagonal tiles are
 // masked element by element.
 //
-// gfx950 mapping (one workgroup = 4 waves = 256 threads):
-//   * A wave owns QB blocks of 32 query rows.  It computes S^T = K Q^T on the
+// gfx950 mapping, common to both kernels below:
+//   * A wave owns blocks of 32 query rows.  It computes S^T = K Q^T on the
 //     32x32x16 MFMA, so a lane holds the scores of ONE query (its column) for
 //     16 of every 32 keys; lane l and lane l^32 share a query.  Row max and
 //     row sum are in-lane plus one exchange with lane l^32.
 //   * Q fragments (the MFMA B operand) sit in VGPRs for the whole K/V loop.
-//   * K and V tiles of BC keys are double-buffered in LDS, row-major with
-//     padded pitches, filled with 16-byte global loads staged in VGPRs while
-//     the previous tile is being consumed.
+//   * K and V tiles of 64 keys are copied global -> LDS with
+//     global_load_lds_dwordx4 (no VGPR staging) into unpadded rows whose
+//     16-byte chunks are XOR-swizzled against bank conflicts, several tiles
+//     ahead of their use.
 //   * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T
 //     accumulators (converted to 16-bit), V^T fragments are read from the
 //     row-major V tile with ds_read_b64_tr_b16 (LDS transpose read).
@@ -32,9 +33,13 @@
 //     the hardware's round-robin dispatch over the 8 XCDs, consecutive
 //     workgroups are different heads of the same query tile, so each XCD keeps
 //     a fixed subset of heads and their K/V stays in that XCD's L2.
+// Two kernels: the key-half unit kernel (8 waves, 256 query rows per
+// workgroup, one workgroup per CU; used when there are enough workgroups of
+// 256 rows) and the ring kernel (4 waves, 128 rows, two workgroups per CU).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
@@ -306,38 +311,60 @@ __device__ __forceinline__ void dma_tile(const u16* __restrict__ src, u16* dst, 
     }
 }
 
-// NW waves of 32 query rows; MINWG workgroups must fit on one CU at once
-// (this bounds the registers per wave).  Tile t lives in stage t % STAGES;
-// during iteration t the copy of tile t + DIST is in flight, and before the
-// iteration's one barrier each wave waits until its own part of tile t + 1
-// has landed.
-//
-// SPLIT (8 waves, two per SIMD): the hardware issues the older of the two
-// waves on a SIMD first, so if both run the same phase at the same time the
-// older one races through its tile and idles at the barrier while the
-// younger finishes alone.  Instead the second wave of each SIMD runs one
-// phase behind: waves 0-3 do QK(t), softmax(t), PV(t) in iteration t while
-// waves 4-7 do softmax(t-1), PV(t-1), QK(t), so one wave's MFMAs meet the
-// other's exponentials.  Waves 4-7 still read V(t-1) in iteration t, so the
-// copy in flight (tile t+2) must not reuse its stage: STAGES = DIST + 2.
-// The tile copies are issued by waves 0-3 only: the lagging waves are on the
-// critical path of every iteration.
-template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, bool SPLIT, int QB>
+// Epilogue: combine the two lane halves of each query's sum; store O = o/l
+// and LSE = (m + log2 l) ln 2 for rows below N, or, for one segment of a key
+// split, the unnormalised o and the (m, l) pair.  Lane (col, g) holds d
+// values 32 mt + 8 i4 + 4 g .. + 3 of query row0[b] + col.
+template <int D, int QB>
+__device__ __forceinline__ void store_rows(const WaveState<D, QB>& st, const AttnArgs& args, int seg,
+                                           int bh, const int* row0, int col, int g) {
+    constexpr int MT = D / 32;
+    const int N = args.N;
+    const bool split = args.part_o != nullptr;
+    const int64_t part = (int64_t)seg * args.BH + bh;
+    float* __restrict__ obase = split ? args.part_o + part * N * D : args.o + (int64_t)bh * N * D;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const float l_tot = st.l[b] + swap32_f32(st.l[b]);
+        const int row = row0[b] + col;
+        if (row >= N) continue;
+        const float inv = split ? 1.0f : 1.0f / l_tot;
+        float* orow = obase + (int64_t)row * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x4 r = {st.acc[b][mt][4 * i4 + 0] * inv, st.acc[b][mt][4 * i4 + 1] * inv,
+                                 st.acc[b][mt][4 * i4 + 2] * inv, st.acc[b][mt][4 * i4 + 3] * inv};
+                *reinterpret_cast<f32x4*>(orow + mt * 32 + 8 * i4 + 4 * g) = r;
+            }
+        if (g == 0) {
+            if (split)
+                args.part_ml[part * N + row] = float2{st.m[b], l_tot};
+            else
+                args.lse[(int64_t)bh * N + row] = (st.m[b] + log2f(l_tot)) * kLn2;
+        }
+    }
+}
+
+// Ring kernel: NW waves of 32 * QB query rows; MINWG workgroups must fit on
+// one CU at once (this bounds the registers per wave).  Tile t lives in stage
+// t % STAGES; during iteration t the copy of tile t + DIST is in flight, and
+// before the iteration's one barrier each wave waits until its own part of
+// tile t + 1 has landed.  Used with 4 waves and two workgroups per CU, where
+// the two waves on a SIMD belong to different workgroups.
+template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, int QB>
 __global__ void __launch_bounds__(64 * NW, MINWG)
 attn_fwd_kernel(AttnArgs args) {
-    using G = Geo<D, NW, STAGES, DIST, SPLIT ? NW / 2 : NW>;
-    static_assert(STAGES >= DIST + (SPLIT ? 2 : 1), "a stage still being read would be overwritten");
-    static_assert(!SPLIT || QB == 1, "the phase split pairs single-block waves");
+    using G = Geo<D, NW, STAGES, DIST, NW>;
+    static_assert(STAGES >= DIST + 1, "a stage still being read would be overwritten");
     constexpr int BR = 32 * QB * NW;   // query rows per workgroup
     __shared__ __attribute__((aligned(1024))) u16 lds[STAGES * G::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Waves w and w + NW/2 share a SIMD; with SPLIT they take adjacent
-    // 32-row blocks so their causal work is equal.
-    const bool lagging = SPLIT && w >= NW / 2;
-    const int block = SPLIT ? 2 * (w % (NW / 2)) + (lagging ? 1 : 0) : w;
+    const int block = w;
 
     const int N = args.N;
     const float scale_log2 = args.scale_log2;
@@ -361,9 +388,6 @@ attn_fwd_kernel(AttnArgs args) {
     const u16* __restrict__ q = args.q + (int64_t)bh * N * D;
     const u16* __restrict__ k = args.k + (int64_t)kvh * N * D;
     const u16* __restrict__ v = args.v + (int64_t)kvh * N * D;
-    float* __restrict__ o = args.o + (int64_t)bh * N * D;
-    float* __restrict__ lse = args.lse + (int64_t)bh * N;
-
     const int row_base = t * BR;
     // Query block b of this wave starts at row0[b]; with QB = 2 the two
     // blocks are adjacent and share their diagonal 64-key tile.
@@ -449,116 +473,465 @@ attn_fwd_kernel(AttnArgs args) {
     // they compute; the loops are split so each holds one code variant.
     f32x16 s[QB][2];
     int it = kt0;
-    if (!lagging) {
-        for (; it < last_live; ++it) {
-            issue(it + DIST);
-            qk(it, s);
-            smpv(it, s);
-            finish(it);
-        }
-        if (it == last_live) {
-            issue(it + DIST);
-            qk(it, s);
-            smpv_last(it, s);
-            finish(it);
-            ++it;
-        }
-    } else {
-        if (last_live >= kt0) {
-            issue(kt0 + DIST);
-            qk(kt0, s);
-            finish(kt0);
-            it = kt0 + 1;
-            for (; it <= last_live; ++it) {
-                issue(it + DIST);
-                smpv(it - 1, s);
-                qk(it, s);
-                finish(it);
-            }
-            if (it < ntiles) {
-                issue(it + DIST);
-                smpv_last(it - 1, s);
-                finish(it);
-                ++it;
-            } else {
-                smpv_last(it - 1, s);  // no copy or barrier left to keep in step with
-            }
-        }
+    for (; it < last_live; ++it) {
+        issue(it + DIST);
+        qk(it, s);
+        smpv(it, s);
+        finish(it);
+    }
+    if (it == last_live) {
+        issue(it + DIST);
+        qk(it, s);
+        smpv_last(it, s);
+        finish(it);
+        ++it;
     }
     for (; it < ntiles; ++it) {
         issue(it + DIST);
         finish(it);
     }
 
-    // Epilogue: combine the two lane halves of each query, normalise, store;
-    // or, for one segment of a key split, store the unnormalised state.
-    if (args.part_o != nullptr) {
-        const int64_t part = (int64_t)seg * args.BH + bh;
-        float* po = args.part_o + part * N * D;
-        float2* pml = args.part_ml + part * N;
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-            const float l_tot = st.l[b] + swap32_f32(st.l[b]);
-            const int row = row0[b] + col;
-            if (row < N) {
-                float* orow = po + (int64_t)row * D;
-#pragma unroll
-                for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4) {
-                        const f32x4 r = {st.acc[b][mt][4 * i4 + 0], st.acc[b][mt][4 * i4 + 1],
-                                         st.acc[b][mt][4 * i4 + 2], st.acc[b][mt][4 * i4 + 3]};
-                        *reinterpret_cast<f32x4*>(orow + mt * 32 + 8 * i4 + 4 * g) = r;
-                    }
-                if (g == 0) pml[row] = float2{st.m[b], l_tot};
-            }
-        }
-        return;
-    }
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-        const float l_tot = st.l[b] + swap32_f32(st.l[b]);
-        const int row = row0[b] + col;
-        if (row < N) {
-            const float inv = 1.0f / l_tot;
-            float* orow = o + (int64_t)row * D;
-#pragma unroll
-            for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x4 r = {st.acc[b][mt][4 * i4 + 0] * inv, st.acc[b][mt][4 * i4 + 1] * inv,
-                                     st.acc[b][mt][4 * i4 + 2] * inv, st.acc[b][mt][4 * i4 + 3] * inv};
-                    *reinterpret_cast<f32x4*>(orow + mt * 32 + 8 * i4 + 4 * g) = r;
-                }
-            if (g == 0) lse[row] = (st.m[b] + log2f(l_tot)) * kLn2;
-        }
-    }
+    store_rows<D, QB>(st, args, seg, bh, row0, col, g);
 }
 
-template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, bool SPLIT,
-          int QB = 1>
-hipError_t launch_one(AttnArgs a, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// Key-half unit kernel: 8 waves of 32 query rows (256 rows per workgroup, one
+// workgroup per CU), two waves per SIMD, all computing.
+//
+// Work is cut into units of one key half (32 keys) of one product:
+// QKa(t), QKb(t) compute S^T for key half 0 / 1 of tile t, and PVa(t), PVb(t)
+// accumulate O^T += V^T P^T for key half 0 / 1.  A wave runs them in the order
+//     X(t) = QKa(t), PVb(t-1)        Y(t) = QKb(t), PVa(t)
+// so the exponentials of a key half are spread over the two units that follow
+// its QK unit: one value per MFMA (fma and exp; every other MFMA a 16-bit pack
+// and a pair sum).  That is three VALU instructions per MFMA, which issue
+// while the wave's own MFMA executes; the work is software-pipelined over the
+// MFMA steps (a value's exp one step after its fma, the pack two steps after,
+// the sum three steps after) so that no instruction waits on one issued
+// beside the same MFMA.  (FA page, section 4: the recurrence; the order of
+// its steps within a tile is unchanged, only their interleaving is.)
+//
+// Reference max and bound.  The exponentials of a key half are taken against
+// the query's current reference max m before that half's scores are
+// examined; the half's sum of P then decides: if every lane's sum is at most
+// 2^8 (so every P is), nothing else is done.  Otherwise each query whose two
+// lanes include such a lane moves m to max(m, the half's max), rescales o and
+// l, and the half's exponentials are taken again.  A query's decision uses
+// only its own scores, so rows never influence each other's bits.  Before the
+// first half no reference exists and the check always fails.
+//
+// Operands stream from LDS through a 4-deep register ring over the fragments
+// of an iteration (K(t) half 0, V(t-1) half 1, K(t) half 1, V(t) half 0).
+// Tile t's V is still read in X(t+1), so a copy may only overwrite a tile two
+// iterations old: K and V each have four stages, copies run two tiles ahead,
+// one barrier per tile.  LDS holds the four K stages, then the four V stages;
+// tile t uses stage (t - kt0) % 4, a compile-time value in the loop unrolled
+// by four, so every fragment address is a per-lane base plus an immediate.
+// Every wave computes every tile of its workgroup: a tile wholly above a
+// wave's rows is fully masked (P = 0 leaves o and l unchanged) and runs while
+// the SIMDs of later rows work on the same tile.
+
+// A key half's P sum at most 2^8 keeps every P of it at most 2^8.
+constexpr float kSumBound = 256.0f;
+
+// P = 2^(s * scale_log2 - m) for the 16 scores of one key half held by this
+// lane, packed to 16-bit MFMA operands (p0: values 0-7, p1: values 8-15);
+// returns the lane's share of the half's sum.  The unit kernel's pipelined
+// exponentials compute exactly this, in this order.
+template <bool BF16>
+__device__ __forceinline__ float half_exp(const f32x16& s, float m, float scale_log2, u32x4& p0,
+                                          u32x4& p1) {
+    using M = Mma<BF16>;
+    float p[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(s[j], scale_log2, -m));
+    p0 = u32x4{M::pack(p[0], p[1]), M::pack(p[2], p[3]), M::pack(p[4], p[5]), M::pack(p[6], p[7])};
+    p1 = u32x4{M::pack(p[8], p[9]), M::pack(p[10], p[11]), M::pack(p[12], p[13]),
+               M::pack(p[14], p[15])};
+    float r0 = 0.0f, r1 = 0.0f;
+    if constexpr (M::kSumRounded) {
+        r0 = M::sum2(p0[0], r0);
+        r1 = M::sum2(p0[1], r1);
+        r0 = M::sum2(p0[2], r0);
+        r1 = M::sum2(p0[3], r1);
+        r0 = M::sum2(p1[0], r0);
+        r1 = M::sum2(p1[1], r1);
+        r0 = M::sum2(p1[2], r0);
+        r1 = M::sum2(p1[3], r1);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+            r0 += p[j];
+            r1 += p[j + 1];
+        }
+    }
+    return r0 + r1;
+}
+
+template <bool BF16, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
+    using G = Geo<D, 8, 4, 2, 8>;
+    using M = Mma<BF16>;
+    constexpr int KS = G::KS;       // K fragments per key half (d steps)
+    constexpr int MT = G::MT;
+    constexpr int NHV = 2 * MT;     // V fragments per key half
+    static_assert(KS == NHV, "QK and PV units have the same number of MFMAs");
+    constexpr int NU = KS;          // MFMAs per unit
+    constexpr int VPQ = 8 / KS;     // hosted values per MFMA step
+    constexpr int TILE = G::TILE;
+    constexpr int BPW = G::BPW;
+    constexpr int NST = 4;          // stages of K and of V
+    constexpr int RING = 4;         // operand fragments in flight
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((address_space(3))) u16 lds_u16;
+    __shared__ __attribute__((aligned(1024))) u16 lds[2 * NST * TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Waves w and w + 4 share a SIMD; they take adjacent 32-row blocks so
+    // their causal work is equal.
+    const int block = 2 * (w & 3) + (w >> 2);
+
+    const int N = args.N;
+    const float scale_log2 = args.scale_log2;
+    // Work item: as in the ring kernel (longest causal tiles first; heads of
+    // one query tile dealt to the 8 XCDs so each XCD keeps a fixed set).
+    const int bid = blockIdx.x;
+    const int per_tile = args.BH * args.nseg;
+    const int tt = bid / per_tile;
+    const int t_q = CAUSAL ? (args.T - 1 - tt) : tt;
+    const int seg = (bid - tt * per_tile) / args.BH;
+    const int j = bid % args.BH;
+    const int bh = (args.BH & 7) ? j : (j & 7) * (args.BH >> 3) + (j >> 3);
+    const int kvh = (bh / args.H) * args.Hkv + (bh % args.H) / (args.H / args.Hkv);
+    const u16* __restrict__ q = args.q + (int64_t)bh * N * D;
+    const u16* __restrict__ k = args.k + (int64_t)kvh * N * D;
+    const u16* __restrict__ v = args.v + (int64_t)kvh * N * D;
+
+    const int row_base = t_q * 256;
+    const int row0 = row_base + block * 32;
+    const int kt0 = seg * args.seg_tiles;
+    const int kv_end = min(CAUSAL ? min(row_base + 256, N) : N, (kt0 + args.seg_tiles) * G::BC);
+    const int ntiles = (kv_end + G::BC - 1) / G::BC;
+    if (kt0 >= ntiles) return;
+    const int T = ntiles - 1;       // last tile
+
+    WaveState<D, 1> st;
+    const int col = lane & 31, g = lane >> 5;
+    {
+        const int row = row0 + col;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            st.qf[0][ks] = row < N ? *reinterpret_cast<const u32x4*>(q + (int64_t)row * D + ks * 16 + 8 * g)
+                                   : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) st.acc[0][mt] = f32x16{};
+        st.m[0] = -INFINITY;
+        st.l[0] = 0.0f;
+    }
+    // Bound on a key half's P sum; negative until the first reference max.
+    float lim = -1.0f;
+
+    // Per-lane LDS fragment bases of stage 0 (pinned so the compiler keeps
+    // base + offset sums out of registers: every offset fits the immediate).
+    const FragOffsets<D> fo = frag_offsets<G>(lane);
+    const lds_u32x4* kp[KS];
+    const lds_s16x4* vp[MT][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        kp[ks] = (const lds_u32x4*)((const lds_u16*)lds + fo.k[ks]);
+        asm volatile("" : "+v"(kp[ks]));
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            vp[mt][r] = (const lds_s16x4*)((const lds_u16*)lds + NST * TILE + fo.v[mt][r]);
+            asm volatile("" : "+v"(vp[mt][r]));
+        }
+    auto k_stage = [&](int s_) __attribute__((always_inline)) { return lds + s_ * TILE; };
+    auto v_stage = [&](int s_) __attribute__((always_inline)) { return lds + (NST + s_) * TILE; };
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        if (t <= T) {
+            const int s_ = (t - kt0) % NST;
+            dma_tile<G>(k, k_stage(s_), t, N, w, lane);
+            dma_tile<G>(v, v_stage(s_), t, N, w, lane);
+        }
+    };
+    // Fragment e of the operand stream of an iteration whose tile is in stage
+    // par: units 0..3 = K(t) half 0, V(t-1) half 1, K(t) half 1, V(t) half 0.
+    // V fragment f of key half kb covers key group 2 kb + f / MT, d block f % MT.
+    auto frag = [&](int par, int e) __attribute__((always_inline)) {
+        const int unit = e / NU, f = e % NU;
+        if (unit == 0 || unit == 2) return kp[f][(par * TILE + (unit / 2) * 32 * D) / 8];
+        const int sp = unit == 1 ? (par + NST - 1) % NST : par;
+        const int kb = unit == 1 ? 1 : 0;
+        const int o = (sp * TILE + (2 * kb + f / MT) * 16 * D) / 4;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp[f % MT][0] + o));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp[f % MT][1] + o));
+        const auto lo = __builtin_bit_cast(unsigned long long, x0);
+        const auto hi = __builtin_bit_cast(unsigned long long, x1);
+        return u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi, (unsigned)(hi >> 32)};
+    };
+
+    f32x16 s[2];        // S^T of key half 0 and 1
+    u32x4 pf[4];        // 16-bit P^T of the four 16-key groups
+    float r0 = 0.0f, r1 = 0.0f;   // the lane's half sum (even / odd pairs)
+    float hx[8], hp[8];
+    unsigned hk[4];
+    // Hosted work: values hi0 .. hi0+7 of key half hkb, VP per MFMA step;
+    // step jstep runs value v's fma when jstep == v / VP, its exp one step
+    // later, the pack of an odd v and its predecessor two steps later and the
+    // pair's sum three steps later.  Steps past the unit's last MFMA drain
+    // after it.  Same arithmetic and order as half_exp.  The empty asm
+    // statements anchor each result where it is computed: the work is pure
+    // and would otherwise sink out of the MFMA stream it fills.
+    auto host_step = [&](int hkb, int hi0, int VP, int jstep) __attribute__((always_inline)) {
+#pragma unroll
+        for (int vv = 0; vv < 8; ++vv) {
+            const int s0 = vv / VP;
+            if (jstep == s0 + 1) {
+                hp[vv] = fast_exp2(hx[vv]);
+                asm volatile("" ::"v"(hp[vv]));
+            }
+            if (jstep == s0) {
+                hx[vv] = fmaf(s[hkb][hi0 + vv], scale_log2, -st.m[0]);
+                asm volatile("" ::"v"(hx[vv]));
+            }
+            if ((vv & 1) && jstep == s0 + 2) {
+                hk[vv >> 1] = M::pack(hp[vv - 1], hp[vv]);
+                asm volatile("" ::"v"(hk[vv >> 1]));
+            }
+            if ((vv & 1) && jstep == s0 + 3) {
+                const int pk_i = (hi0 + vv) >> 1;   // pair index within the half
+                if constexpr (M::kSumRounded) {
+                    if (pk_i & 1)
+                        r1 = M::sum2(hk[vv >> 1], r1);
+                    else
+                        r0 = M::sum2(hk[vv >> 1], r0);
+                } else {
+                    r0 += hp[vv - 1];
+                    r1 += hp[vv];
+                }
+                asm volatile("" ::"v"(r0), "v"(r1));
+                pf[2 * hkb + pk_i / 4][pk_i % 4] = hk[vv >> 1];
+            }
+        }
+    };
+    auto host_drain = [&](int hkb, int hi0, int VP, int from) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jstep = from; jstep < 8 / VP + 3; ++jstep) host_step(hkb, hi0, VP, jstep);
+    };
+    // Scores of keys after the query (causal) or past N set to -inf.  Lane
+    // (col, g) holds keys 8(i/4) + 4g + i%4 of key half kb for query row0 + col.
+    auto mask_half = [&](int kb, int key0) __attribute__((always_inline)) {
+        const int lim_c = min(CAUSAL ? row0 + col - key0 : (1 << 30), N - 1 - key0) - 4 * g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int c = kb * 32 + 8 * (i >> 2) + (i & 3);
+            s[kb][i] = c > lim_c ? -INFINITY : s[kb][i];
+        }
+    };
+    auto is_masked = [&](int t) __attribute__((always_inline)) {
+        const int key0 = t * G::BC;
+        return (CAUSAL && key0 + G::BC - 1 > row0) || key0 + G::BC > N;
+    };
+    // Key half kb's exponentials are complete: the bound check, the rare
+    // move of the reference max, and the half's sum into l.
+    auto settle = [&](int kb) __attribute__((always_inline)) {
+        float rs = r0 + r1;
+        r0 = 0.0f;
+        r1 = 0.0f;
+        if (__builtin_amdgcn_ballot_w64(!(rs <= lim)) != 0) {
+            // Both lanes of a query take the same decision; the exchanges run
+            // in every lane (under a partial EXEC mask they would read stale
+            // values).
+            const float rs_pair = swap32_f32(rs);
+            const bool need = !(rs <= lim && rs_pair <= lim);
+            float hm = s[kb][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) hm = fmaxf(hm, s[kb][i]);
+            hm = fmaxf(hm, swap32_f32(hm)) * scale_log2;
+            const float m_new = need ? fmaxf(st.m[0], hm) : st.m[0];
+            const float alpha = need ? online_rescale(st.m[0], m_new) : 1.0f;
+            st.l[0] *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) st.acc[0][mt] *= alpha;
+            st.m[0] = m_new;
+            rs = half_exp<BF16>(s[kb], m_new, scale_log2, pf[2 * kb], pf[2 * kb + 1]);
+            lim = kSumBound;
+        }
+        st.l[0] += rs;
+    };
+
+    // One iteration: the fragment stream through the ring, one loop per
+    // unit, with the settle and mask steps between units.  HEAD (t = kt0):
+    // there is no PVb(t-1); half 0's first exponentials run alone.
+    auto iteration = [&](auto par_c, auto head_c, int t) __attribute__((always_inline)) {
+        constexpr int par = decltype(par_c)::value;
+        constexpr bool HEAD = decltype(head_c)::value;
+        u32x4 ring[RING];
+        // Stream position i fragments after (unit u, fragment f); HEAD skips
+        // unit 1.  At or past 4 * NU: beyond this iteration.
+        auto ahead = [&](int u, int f, int i) __attribute__((always_inline)) {
+            int uu = u, ff = f + i;
+            while (ff >= NU && uu < 4) {
+                ff -= NU;
+                uu = (HEAD && uu == 0) ? 2 : uu + 1;
+            }
+            return uu * NU + ff;
+        };
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < RING; ++i) ring[i] = frag(par, ahead(0, 0, i));
+        int rslot = 0;
+        auto unit_loop = [&](auto u_c) __attribute__((always_inline)) {
+            constexpr int u = decltype(u_c)::value;
+#pragma unroll
+            for (int f = 0; f < NU; ++f) {
+                const u32x4 a = ring[(rslot + f) % RING];
+                if constexpr (u == 0 || u == 2) {
+                    if (f == 0) s[u / 2] = f32x16{};
+                    s[u / 2] = M::run(a, st.qf[0][f], s[u / 2]);
+                } else {
+                    const int kb = u == 1 ? 1 : 0;
+                    st.acc[0][f % MT] = M::run(a, pf[2 * kb + f / MT], st.acc[0][f % MT]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const int e = ahead(u, f, RING);
+                if (e < 4 * NU) ring[(rslot + f) % RING] = frag(par, e);
+                // X: QKa hosts values 8..15 of half 1 (tile t-1), PVb values
+                // 0..7 of half 0; Y: QKb hosts values 8..15 of half 0, PVa
+                // values 0..7 of half 1.
+                if constexpr (u == 0) {
+                    if (!HEAD) host_step(1, 8, VPQ, f);
+                } else if constexpr (u == 1) {
+                    host_step(0, 0, VPQ, f);
+                } else if constexpr (u == 2) {
+                    host_step(0, 8, VPQ, f);
+                } else {
+                    host_step(1, 0, VPQ, f);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            rslot = (rslot + NU) % RING;
+        };
+        unit_loop(std::integral_constant<int, 0>{});
+        if (!HEAD) {
+            host_drain(1, 8, VPQ, NU);
+            settle(1);
+        }
+        if (is_masked(t)) mask_half(0, t * G::BC);
+        if (HEAD) {
+            host_drain(0, 0, 1, 0);
+        } else {
+            unit_loop(std::integral_constant<int, 1>{});
+            host_drain(0, 0, VPQ, NU);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        unit_loop(std::integral_constant<int, 2>{});
+        host_drain(0, 8, VPQ, NU);
+        settle(0);
+        if (is_masked(t)) mask_half(1, t * G::BC);
+        __builtin_amdgcn_sched_barrier(0);
+        unit_loop(std::integral_constant<int, 3>{});
+        host_drain(1, 0, VPQ, NU);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // End of iteration t: tile t+1 complete for this wave (the copy of t+2
+    // may still fly), then the barrier makes it complete for all.
+    auto finish = [&](int t) __attribute__((always_inline)) {
+        if (t + 2 <= T)
+            wait_vmcnt<2 * BPW>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+    };
+
+    // Prologue: the first two tiles are copied while the Q fragments arrive;
+    // one full wait covers both (and tells the compiler Q is ready).
+    issue(kt0);
+    issue(kt0 + 1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    issue(kt0 + 2);
+    iteration(P0{}, std::true_type{}, kt0);
+    finish(kt0);
+    auto step = [&](auto par_c, int t) __attribute__((always_inline)) {
+        issue(t + 2);
+        iteration(par_c, std::false_type{}, t);
+        finish(t);
+    };
+    // Tiles kt0+1 .. T (stages 1, 2, 3, 0, ...) in groups of four, then the
+    // remainder: the loop keeps a single exit (a second exit gave the O
+    // accumulators two register homes).
+    const int nmain = T - kt0;
+    const int nq = nmain / 4;
+    int t = kt0 + 1;
+    for (int i = 0; i < nq; ++i, t += 4) {
+        step(P1{}, t);
+        step(P2{}, t + 1);
+        step(P3{}, t + 2);
+        step(P0{}, t + 3);
+    }
+    const int nr = nmain - 4 * nq;
+    if (nr >= 1) step(P1{}, t++);
+    if (nr >= 2) step(P2{}, t++);
+    if (nr >= 3) step(P3{}, t++);
+    // Tail: half 1 of tile T (exponentials, settle, PVb(T)).
+    {
+        host_drain(1, 8, 1, 0);
+        settle(1);
+        const u16* vt = v_stage((T - kt0) % NST);
+#pragma unroll
+        for (int f = 0; f < NHV; ++f) {
+            const u16* base = vt + (2 + f / MT) * 16 * D;
+            const u32x4 a = tr16_b64x2(base + fo.v[f % MT][0], base + fo.v[f % MT][1]);
+            st.acc[0][f % MT] = M::run(a, pf[2 + f / MT], st.acc[0][f % MT]);
+        }
+    }
+
+    store_rows<D, 1>(st, args, seg, bh, &row0, col, g);
+}
+
+template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, int QB = 1>
+hipError_t launch_ring(AttnArgs a, hipStream_t stream) {
     constexpr int BR = 32 * QB * NW;
     a.T = (a.N + BR - 1) / BR;
     a.scale_log2 = kLog2e / __builtin_sqrtf((float)D);
     void* params[] = {(void*)&a};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, NW, MINWG, STAGES, DIST, SPLIT, QB>),
+        reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, NW, MINWG, STAGES, DIST, QB>),
         dim3((unsigned)(a.T * a.BH * a.nseg)), dim3(64 * NW), params, 0, stream);
 }
 
-// 8 waves, one workgroup per CU, phase-split, copies two tiles ahead (four
-// stages); or 4 waves, two independent workgroups per CU (LDS for two: copies
-// one tile ahead at D = 128, two at D = 64).
+template <bool BF16, int D, bool CAUSAL>
+hipError_t launch_units(AttnArgs a, hipStream_t stream) {
+    a.T = (a.N + 255) / 256;
+    a.scale_log2 = kLog2e / __builtin_sqrtf((float)D);
+    void* params[] = {(void*)&a};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_units_kernel<BF16, D, CAUSAL>),
+                           dim3((unsigned)(a.T * a.BH * a.nseg)), dim3(512), params, 0, stream);
+}
+
+// 8 waves: the key-half unit kernel (256 query rows, one workgroup per CU).
+// 4 waves: the ring kernel, two workgroups per CU (LDS for two: copies one
+// tile ahead at D = 128, two at D = 64).
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_cfg(const AttnArgs& a, int waves, hipStream_t stream) {
     if (waves == 4) {
         if constexpr (D == 128)
-            return launch_one<BF16, D, CAUSAL, 4, 2, 2, 1, false>(a, stream);
+            return launch_ring<BF16, D, CAUSAL, 4, 2, 2, 1>(a, stream);
         else
-            return launch_one<BF16, D, CAUSAL, 4, 2, 3, 2, false>(a, stream);
+            return launch_ring<BF16, D, CAUSAL, 4, 2, 3, 2>(a, stream);
     }
-    return launch_one<BF16, D, CAUSAL, 8, 1, 4, 2, true>(a, stream);
+    return launch_units<BF16, D, CAUSAL>(a, stream);
 }
 
 }  // namespace

@@ -149,3 +149,55 @@ def test_identical_keys_give_prefix_mean_on_gpu():
     mean = np.cumsum(vv, axis=0) / np.arange(1, N + 1)[:, None]
     assert np.abs(o[0, 0] - mean).max() <= tolerances.ATTN_O["bf16"]
     assert np.abs(lse[0, 0] - np.log(np.arange(1, N + 1))).max() <= tolerances.ATTN_LSE
+
+
+# Shapes with B*H*ceil(N/256) >= 512 run 8-wave workgroups of 256 query rows
+# (the key-half unit kernel); the small shapes above run 4-wave workgroups.
+WIDE = [
+    # (B, H, N, D, sigma_qk)
+    (1, 512, 64, 128, 1.0),     # one 64-key tile per head
+    (1, 512, 200, 64, 1.5),     # one partial query tile per head
+    (2, 128, 300, 128, 3.0),    # ragged second tile; large logits
+    (1, 256, 513, 64, 3.0),     # one row past a 256-row tile edge
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: "B%dH%dN%dD%ds%g" % s)
+def test_wide_shapes_match_oracle(shape, causal, dtype):
+    B, H, N, D, sigma = shape
+    assert B * H * ((N + 255) // 256) >= 512
+    seed = 2000 + N * 7 + D + (1 if causal else 0)
+    q, k, v = workloads.attn_inputs(B, H, N, D, dtype, seed, sigma_qk=sigma)
+    name = "wide attn %s %s B%d H%d N%d D%d sigma %g seed %d" % (
+        "causal" if causal else "full", dtype, B, H, N, D, sigma, seed)
+    print("running", name, flush=True)
+    o, lse = run_gpu(q, k, v, causal, dtype)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal)
+    check(name, o, lse, o_ref, lse_ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_wide_ramped_logits(causal, dtype):
+    """Scores that rise (or fall) steeply along the keys: with q near 1 and
+    k_j near slope_h * j, every key half of a rising head holds a new row
+    maximum far above the previous one, so the reference maximum has to move
+    for every half; falling heads never move it after the first key; flat and
+    noisy heads sit in between.  Scaled logits reach several hundred."""
+    B, H, N, D = 1, 512, 256, 64
+    g = torch.Generator().manual_seed(2301)
+    slopes = torch.tensor([0.05, -0.05, 0.3, 0.0, 0.02, -0.3, 0.15, 0.01])
+    slope = slopes[torch.arange(H) % len(slopes)].view(1, H, 1, 1)
+    j = torch.arange(N, dtype=torch.float32).view(1, 1, N, 1)
+    td = workloads.TORCH_DTYPE[dtype]
+    q = (1.0 + 0.1 * torch.randn((B, H, N, D), generator=g)).to(td).contiguous()
+    k = (slope * j + 0.5 * torch.randn((B, H, N, D), generator=g)).to(td).contiguous()
+    v = torch.randn((B, H, N, D), generator=g).to(td).contiguous()
+    name = "wide ramped logits %s %s B1 H512 N256 D64" % ("causal" if causal else "full", dtype)
+    print("running", name, flush=True)
+    o, lse = run_gpu(q, k, v, causal, dtype)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal)
+    assert np.abs(lse_ref).max() > 300.0
+    check(name, o, lse, o_ref, lse_ref, dtype)
