@@ -298,17 +298,21 @@ __device__ __forceinline__ void softmax_pv_tile(WaveState<G::D, QB>& st, const F
 // head's K (or V) into an LDS tile.  Rows past N are clamped to row N-1: they
 // only feed keys that are masked (score -inf, weight exactly 0).
 template <class G>
+__device__ __forceinline__ void dma_block(const u16* __restrict__ src, u16* dst, int tile, int N,
+                                          int w, int lane, int j) {
+    constexpr int D = G::D;
+    const int blk = w * G::BPW + j;
+    const int r = blk * G::RPB + lane / G::CPR;
+    const int c = (lane % G::CPR) ^ chunk_swizzle<D>(r);
+    const int key = min(tile * G::BC + r, N - 1);
+    copy_to_lds16(src, (unsigned)((key * D + c * 8) * 2), dst + blk * 512);
+}
+
+template <class G>
 __device__ __forceinline__ void dma_tile(const u16* __restrict__ src, u16* dst, int tile, int N,
                                          int w, int lane) {
-    constexpr int D = G::D;
 #pragma unroll
-    for (int j = 0; j < G::BPW; ++j) {
-        const int blk = w * G::BPW + j;
-        const int r = blk * G::RPB + lane / G::CPR;
-        const int c = (lane % G::CPR) ^ chunk_swizzle<D>(r);
-        const int key = min(tile * G::BC + r, N - 1);
-        copy_to_lds16(src, (unsigned)((key * D + c * 8) * 2), dst + blk * 512);
-    }
+    for (int j = 0; j < G::BPW; ++j) dma_block<G>(src, dst, tile, N, w, lane, j);
 }
 
 // Epilogue: combine the two lane halves of each query's sum; store O = o/l
@@ -568,16 +572,18 @@ __device__ __forceinline__ float half_exp(const f32x16& s, float m, float scale_
     return r0 + r1;
 }
 
-template <bool BF16, int D, bool CAUSAL>
-__global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
-    using G = Geo<D, 8, 4, 2, 8>;
+template <bool BF16, int D, bool CAUSAL, int QB, int NWV>
+__global__ void __launch_bounds__(64 * NWV, 1) attn_fwd_units_kernel(AttnArgs args) {
+    using G = Geo<D, NWV, 4, 2, NWV>;
     using M = Mma<BF16>;
     constexpr int KS = G::KS;       // K fragments per key half (d steps)
     constexpr int MT = G::MT;
     constexpr int NHV = 2 * MT;     // V fragments per key half
     static_assert(KS == NHV, "QK and PV units have the same number of MFMAs");
-    constexpr int NU = KS;          // MFMAs per unit
+    constexpr int NU = KS;          // operand fragments per unit (each feeds QB MFMAs)
     constexpr int VPQ = 8 / KS;     // hosted values per MFMA step
+    constexpr int HV = 8 * QB;      // hosted values per unit
+    constexpr int RW = 32 * QB * NWV;   // query rows per workgroup
     constexpr int TILE = G::TILE;
     constexpr int BPW = G::BPW;
     constexpr int NST = 4;          // stages of K and of V
@@ -590,9 +596,9 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Waves w and w + 4 share a SIMD; they take adjacent 32-row blocks so
-    // their causal work is equal.
-    const int block = 2 * (w & 3) + (w >> 2);
+    // Waves w and w + 4 share a SIMD; they take adjacent row spans so their
+    // causal work is equal.  A wave owns QB adjacent 32-row blocks.
+    const int block = NWV == 8 ? 2 * (w & 3) + (w >> 2) : w;
 
     const int N = args.N;
     const float scale_log2 = args.scale_log2;
@@ -610,26 +616,29 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
     const u16* __restrict__ k = args.k + (int64_t)kvh * N * D;
     const u16* __restrict__ v = args.v + (int64_t)kvh * N * D;
 
-    const int row_base = t_q * 256;
-    const int row0 = row_base + block * 32;
+    const int row_base = t_q * RW;
+    int row0[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) row0[b] = row_base + (QB * block + b) * 32;
     const int kt0 = seg * args.seg_tiles;
-    const int kv_end = min(CAUSAL ? min(row_base + 256, N) : N, (kt0 + args.seg_tiles) * G::BC);
+    const int kv_end = min(CAUSAL ? min(row_base + RW, N) : N, (kt0 + args.seg_tiles) * G::BC);
     const int ntiles = (kv_end + G::BC - 1) / G::BC;
     if (kt0 >= ntiles) return;
     const int T = ntiles - 1;       // last tile
 
-    WaveState<D, 1> st;
+    WaveState<D, QB> st;
     const int col = lane & 31, g = lane >> 5;
-    {
-        const int row = row0 + col;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const int row = row0[b] + col;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            st.qf[0][ks] = row < N ? *reinterpret_cast<const u32x4*>(q + (int64_t)row * D + ks * 16 + 8 * g)
+            st.qf[b][ks] = row < N ? *reinterpret_cast<const u32x4*>(q + (int64_t)row * D + ks * 16 + 8 * g)
                                    : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) st.acc[0][mt] = f32x16{};
-        st.m[0] = -INFINITY;
-        st.l[0] = 0.0f;
+        for (int mt = 0; mt < MT; ++mt) st.acc[b][mt] = f32x16{};
+        st.m[b] = -INFINITY;
+        st.l[b] = 0.0f;
     }
     // Bound on a key half's P sum; negative until the first reference max.
     float lim = -1.0f;
@@ -660,6 +669,23 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
             dma_tile<G>(v, v_stage(s_), t, N, w, lane);
         }
     };
+    // The same copies spread over the four units of an iteration (copy i of
+    // the wave's 2 * BPW goes with unit 4 i / (2 BPW)): issued together after
+    // the barrier, the copies of all waves queued behind each other and held
+    // the waves' first MFMAs back.
+    auto issue_part = [&](int t, int u) __attribute__((always_inline)) {
+        if (t <= T) {
+            const int s_ = (t - kt0) % NST;
+#pragma unroll
+            for (int i = 0; i < 2 * BPW; ++i) {
+                if ((4 * i) / (2 * BPW) != u) continue;
+                if (i < BPW)
+                    dma_block<G>(k, k_stage(s_), t, N, w, lane, i);
+                else
+                    dma_block<G>(v, v_stage(s_), t, N, w, lane, i - BPW);
+            }
+        }
+    };
     // Fragment e of the operand stream of an iteration whose tile is in stage
     // par: units 0..3 = K(t) half 0, V(t-1) half 1, K(t) half 1, V(t) half 0.
     // V fragment f of key half kb covers key group 2 kb + f / MT, d block f % MT.
@@ -676,28 +702,32 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
         return u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi, (unsigned)(hi >> 32)};
     };
 
-    f32x16 s[2];        // S^T of key half 0 and 1
-    u32x4 pf[4];        // 16-bit P^T of the four 16-key groups
-    float r0 = 0.0f, r1 = 0.0f;   // the lane's half sum (even / odd pairs)
-    float hx[8], hp[8];
-    unsigned hk[4];
-    // Hosted work: values hi0 .. hi0+7 of key half hkb, VP per MFMA step;
-    // step jstep runs value v's fma when jstep == v / VP, its exp one step
-    // later, the pack of an odd v and its predecessor two steps later and the
-    // pair's sum three steps later.  Steps past the unit's last MFMA drain
-    // after it.  Same arithmetic and order as half_exp.  The empty asm
-    // statements anchor each result where it is computed: the work is pure
-    // and would otherwise sink out of the MFMA stream it fills.
+    f32x16 s[2][QB];    // S^T of key half 0 and 1, per row block
+    u32x4 pf[QB][4];    // 16-bit P^T of the four 16-key groups, per row block
+    float r0[QB], r1[QB];   // the lane's half sums (even / odd pairs)
+#pragma unroll
+    for (int b = 0; b < QB; ++b) r0[b] = r1[b] = 0.0f;
+    float hx[HV], hp[HV];
+    unsigned hk[HV / 2];
+    // Hosted work: values hi0 .. hi0+7 of key half hkb of each row block
+    // (value vv: row block vv / 8), VP per MFMA step; step jstep runs value
+    // vv's fma when jstep == vv / VP, its exp one step later, the pack of an
+    // odd vv and its predecessor two steps later and the pair's sum three
+    // steps later.  Steps past the unit's last MFMA drain after it.  Same
+    // arithmetic and order as half_exp.  The empty asm statements anchor each
+    // result where it is computed: the work is pure and would otherwise sink
+    // out of the MFMA stream it fills.
     auto host_step = [&](int hkb, int hi0, int VP, int jstep) __attribute__((always_inline)) {
 #pragma unroll
-        for (int vv = 0; vv < 8; ++vv) {
+        for (int vv = 0; vv < HV; ++vv) {
+            const int b = vv / 8, idx = hi0 + vv % 8;
             const int s0 = vv / VP;
             if (jstep == s0 + 1) {
                 hp[vv] = fast_exp2(hx[vv]);
                 asm volatile("" ::"v"(hp[vv]));
             }
             if (jstep == s0) {
-                hx[vv] = fmaf(s[hkb][hi0 + vv], scale_log2, -st.m[0]);
+                hx[vv] = fmaf(s[hkb][b][idx], scale_log2, -st.m[b]);
                 asm volatile("" ::"v"(hx[vv]));
             }
             if ((vv & 1) && jstep == s0 + 2) {
@@ -705,65 +735,79 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
                 asm volatile("" ::"v"(hk[vv >> 1]));
             }
             if ((vv & 1) && jstep == s0 + 3) {
-                const int pk_i = (hi0 + vv) >> 1;   // pair index within the half
+                const int pk_i = idx >> 1;   // pair index within the half
                 if constexpr (M::kSumRounded) {
                     if (pk_i & 1)
-                        r1 = M::sum2(hk[vv >> 1], r1);
+                        r1[b] = M::sum2(hk[vv >> 1], r1[b]);
                     else
-                        r0 = M::sum2(hk[vv >> 1], r0);
+                        r0[b] = M::sum2(hk[vv >> 1], r0[b]);
                 } else {
-                    r0 += hp[vv - 1];
-                    r1 += hp[vv];
+                    r0[b] += hp[vv - 1];
+                    r1[b] += hp[vv];
                 }
-                asm volatile("" ::"v"(r0), "v"(r1));
-                pf[2 * hkb + pk_i / 4][pk_i % 4] = hk[vv >> 1];
+                asm volatile("" ::"v"(r0[b]), "v"(r1[b]));
+                pf[b][2 * hkb + pk_i / 4][pk_i % 4] = hk[vv >> 1];
             }
         }
     };
     auto host_drain = [&](int hkb, int hi0, int VP, int from) __attribute__((always_inline)) {
 #pragma unroll
-        for (int jstep = from; jstep < 8 / VP + 3; ++jstep) host_step(hkb, hi0, VP, jstep);
+        for (int jstep = from; jstep < HV / VP + 3; ++jstep) host_step(hkb, hi0, VP, jstep);
     };
     // Scores of keys after the query (causal) or past N set to -inf.  Lane
-    // (col, g) holds keys 8(i/4) + 4g + i%4 of key half kb for query row0 + col.
+    // (col, g) holds keys 8(i/4) + 4g + i%4 of key half kb for query
+    // row0[b] + col.
     auto mask_half = [&](int kb, int key0) __attribute__((always_inline)) {
-        const int lim_c = min(CAUSAL ? row0 + col - key0 : (1 << 30), N - 1 - key0) - 4 * g;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int c = kb * 32 + 8 * (i >> 2) + (i & 3);
-            s[kb][i] = c > lim_c ? -INFINITY : s[kb][i];
+        for (int b = 0; b < QB; ++b) {
+            const int lim_c = min(CAUSAL ? row0[b] + col - key0 : (1 << 30), N - 1 - key0) - 4 * g;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int c = kb * 32 + 8 * (i >> 2) + (i & 3);
+                s[kb][b][i] = c > lim_c ? -INFINITY : s[kb][b][i];
+            }
         }
     };
     auto is_masked = [&](int t) __attribute__((always_inline)) {
         const int key0 = t * G::BC;
-        return (CAUSAL && key0 + G::BC - 1 > row0) || key0 + G::BC > N;
+        return (CAUSAL && key0 + G::BC - 1 > row0[0]) || key0 + G::BC > N;
     };
     // Key half kb's exponentials are complete: the bound check, the rare
     // move of the reference max, and the half's sum into l.
     auto settle = [&](int kb) __attribute__((always_inline)) {
-        float rs = r0 + r1;
-        r0 = 0.0f;
-        r1 = 0.0f;
-        if (__builtin_amdgcn_ballot_w64(!(rs <= lim)) != 0) {
-            // Both lanes of a query take the same decision; the exchanges run
-            // in every lane (under a partial EXEC mask they would read stale
-            // values).
-            const float rs_pair = swap32_f32(rs);
-            const bool need = !(rs <= lim && rs_pair <= lim);
-            float hm = s[kb][0];
+        float rs[QB];
+        bool bad = false;
 #pragma unroll
-            for (int i = 1; i < 16; ++i) hm = fmaxf(hm, s[kb][i]);
-            hm = fmaxf(hm, swap32_f32(hm)) * scale_log2;
-            const float m_new = need ? fmaxf(st.m[0], hm) : st.m[0];
-            const float alpha = need ? online_rescale(st.m[0], m_new) : 1.0f;
-            st.l[0] *= alpha;
+        for (int b = 0; b < QB; ++b) {
+            rs[b] = r0[b] + r1[b];
+            r0[b] = 0.0f;
+            r1[b] = 0.0f;
+            bad = bad || !(rs[b] <= lim);
+        }
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) st.acc[0][mt] *= alpha;
-            st.m[0] = m_new;
-            rs = half_exp<BF16>(s[kb], m_new, scale_log2, pf[2 * kb], pf[2 * kb + 1]);
+            for (int b = 0; b < QB; ++b) {
+                // Both lanes of a query take the same decision; the exchanges
+                // run in every lane (under a partial EXEC mask they would read
+                // stale values).
+                const float rs_pair = swap32_f32(rs[b]);
+                const bool need = !(rs[b] <= lim && rs_pair <= lim);
+                float hm = s[kb][b][0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) hm = fmaxf(hm, s[kb][b][i]);
+                hm = fmaxf(hm, swap32_f32(hm)) * scale_log2;
+                const float m_new = need ? fmaxf(st.m[b], hm) : st.m[b];
+                const float alpha = need ? online_rescale(st.m[b], m_new) : 1.0f;
+                st.l[b] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) st.acc[b][mt] *= alpha;
+                st.m[b] = m_new;
+                rs[b] = half_exp<BF16>(s[kb][b], m_new, scale_log2, pf[b][2 * kb], pf[b][2 * kb + 1]);
+            }
             lim = kSumBound;
         }
-        st.l[0] += rs;
+#pragma unroll
+        for (int b = 0; b < QB; ++b) st.l[b] += rs[b];
     };
 
     // One iteration: the fragment stream through the ring, one loop per
@@ -792,35 +836,42 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
 #pragma unroll
             for (int f = 0; f < NU; ++f) {
                 const u32x4 a = ring[(rslot + f) % RING];
-                if constexpr (u == 0 || u == 2) {
-                    if (f == 0) s[u / 2] = f32x16{};
-                    s[u / 2] = M::run(a, st.qf[0][f], s[u / 2]);
-                } else {
-                    const int kb = u == 1 ? 1 : 0;
-                    st.acc[0][f % MT] = M::run(a, pf[2 * kb + f / MT], st.acc[0][f % MT]);
+#pragma unroll
+                for (int b = 0; b < QB; ++b) {
+                    if constexpr (u == 0 || u == 2) {
+                        if (f == 0) s[u / 2][b] = f32x16{};
+                        s[u / 2][b] = M::run(a, st.qf[b][f], s[u / 2][b]);
+                    } else {
+                        const int kb = u == 1 ? 1 : 0;
+                        st.acc[b][f % MT] = M::run(a, pf[b][2 * kb + f / MT], st.acc[b][f % MT]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (b == 0) {
+                        const int e = ahead(u, f, RING);
+                        if (e < 4 * NU) ring[(rslot + f) % RING] = frag(par, e);
+                        if (!HEAD && f == 0) issue_part(t + 2, u);
+                    }
+                    // X: QKa hosts values 8..15 of half 1 (tile t-1), PVb
+                    // values 0..7 of half 0; Y: QKb hosts values 8..15 of
+                    // half 0, PVa values 0..7 of half 1.
+                    const int js = f * QB + b;
+                    if constexpr (u == 0) {
+                        if (!HEAD) host_step(1, 8, VPQ, js);
+                    } else if constexpr (u == 1) {
+                        host_step(0, 0, VPQ, js);
+                    } else if constexpr (u == 2) {
+                        host_step(0, 8, VPQ, js);
+                    } else {
+                        host_step(1, 0, VPQ, js);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                const int e = ahead(u, f, RING);
-                if (e < 4 * NU) ring[(rslot + f) % RING] = frag(par, e);
-                // X: QKa hosts values 8..15 of half 1 (tile t-1), PVb values
-                // 0..7 of half 0; Y: QKb hosts values 8..15 of half 0, PVa
-                // values 0..7 of half 1.
-                if constexpr (u == 0) {
-                    if (!HEAD) host_step(1, 8, VPQ, f);
-                } else if constexpr (u == 1) {
-                    host_step(0, 0, VPQ, f);
-                } else if constexpr (u == 2) {
-                    host_step(0, 8, VPQ, f);
-                } else {
-                    host_step(1, 0, VPQ, f);
-                }
-                __builtin_amdgcn_sched_barrier(0);
             }
             rslot = (rslot + NU) % RING;
         };
         unit_loop(std::integral_constant<int, 0>{});
         if (!HEAD) {
-            host_drain(1, 8, VPQ, NU);
+            host_drain(1, 8, VPQ, NU * QB);
             settle(1);
         }
         if (is_masked(t)) mask_half(0, t * G::BC);
@@ -828,16 +879,16 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
             host_drain(0, 0, 1, 0);
         } else {
             unit_loop(std::integral_constant<int, 1>{});
-            host_drain(0, 0, VPQ, NU);
+            host_drain(0, 0, VPQ, NU * QB);
         }
         __builtin_amdgcn_sched_barrier(0);
         unit_loop(std::integral_constant<int, 2>{});
-        host_drain(0, 8, VPQ, NU);
+        host_drain(0, 8, VPQ, NU * QB);
         settle(0);
         if (is_masked(t)) mask_half(1, t * G::BC);
         __builtin_amdgcn_sched_barrier(0);
         unit_loop(std::integral_constant<int, 3>{});
-        host_drain(1, 0, VPQ, NU);
+        host_drain(1, 0, VPQ, NU * QB);
         __builtin_amdgcn_sched_barrier(0);
     };
     // End of iteration t: tile t+1 complete for this wave (the copy of t+2
@@ -864,7 +915,6 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
     iteration(P0{}, std::true_type{}, kt0);
     finish(kt0);
     auto step = [&](auto par_c, int t) __attribute__((always_inline)) {
-        issue(t + 2);
         iteration(par_c, std::false_type{}, t);
         finish(t);
     };
@@ -893,11 +943,13 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_units_kernel(AttnArgs args) {
         for (int f = 0; f < NHV; ++f) {
             const u16* base = vt + (2 + f / MT) * 16 * D;
             const u32x4 a = tr16_b64x2(base + fo.v[f % MT][0], base + fo.v[f % MT][1]);
-            st.acc[0][f % MT] = M::run(a, pf[2 + f / MT], st.acc[0][f % MT]);
+#pragma unroll
+            for (int b = 0; b < QB; ++b)
+                st.acc[b][f % MT] = M::run(a, pf[b][2 + f / MT], st.acc[b][f % MT]);
         }
     }
 
-    store_rows<D, 1>(st, args, seg, bh, &row0, col, g);
+    store_rows<D, QB>(st, args, seg, bh, row0, col, g);
 }
 
 template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, int QB = 1>
@@ -911,13 +963,27 @@ hipError_t launch_ring(AttnArgs a, hipStream_t stream) {
         dim3((unsigned)(a.T * a.BH * a.nseg)), dim3(64 * NW), params, 0, stream);
 }
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool CAUSAL, int QB, int NWV>
 hipError_t launch_units(AttnArgs a, hipStream_t stream) {
-    a.T = (a.N + 255) / 256;
+    constexpr int RW = 32 * QB * NWV;
+    a.T = (a.N + RW - 1) / RW;
     a.scale_log2 = kLog2e / __builtin_sqrtf((float)D);
     void* params[] = {(void*)&a};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_units_kernel<BF16, D, CAUSAL>),
-                           dim3((unsigned)(a.T * a.BH * a.nseg)), dim3(512), params, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_units_kernel<BF16, D, CAUSAL, QB, NWV>),
+                           dim3((unsigned)(a.T * a.BH * a.nseg)), dim3(64 * NWV), params, 0, stream);
+}
+
+// Two 32-row blocks per wave (512 query rows per workgroup) at D = 64 when
+// that still gives two workgroups per CU: each K/V fragment read from LDS
+// then feeds two MFMAs.  (At D = 128 the two blocks' O accumulators, Q
+// fragments and scores exceed the 256 registers a wave has at two waves per
+// SIMD.)
+inline bool units_qb2(int64_t BH, int64_t N) {
+#ifdef OSC_QB2_MIN
+    return BH * ((N + 511) / 512) >= OSC_QB2_MIN;
+#else
+    return BH * ((N + 511) / 512) >= 512;
+#endif
 }
 
 // 8 waves: the key-half unit kernel (256 query rows, one workgroup per CU).
@@ -931,7 +997,14 @@ hipError_t launch_cfg(const AttnArgs& a, int waves, hipStream_t stream) {
         else
             return launch_ring<BF16, D, CAUSAL, 4, 2, 3, 2>(a, stream);
     }
-    return launch_units<BF16, D, CAUSAL>(a, stream);
+    if constexpr (D == 64) {
+        if (a.nseg == 1 && units_qb2(a.BH, a.N)) return launch_units<BF16, D, CAUSAL, 2, 8>(a, stream);
+    } else {
+#ifdef OSC_D128_QB2W4
+        if (a.nseg == 1) return launch_units<BF16, D, CAUSAL, 2, 4>(a, stream);
+#endif
+    }
+    return launch_units<BF16, D, CAUSAL, 1, 8>(a, stream);
 }
 
 }  // namespace
