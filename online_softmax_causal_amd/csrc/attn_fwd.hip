@@ -308,6 +308,19 @@ __device__ __forceinline__ void dma_block(const u16* __restrict__ src, u16* dst,
     copy_to_lds16(src, (unsigned)((key * D + c * 8) * 2), dst + blk * 512);
 }
 
+// The same for a tile wholly below N: nothing to clamp, so each lane's offset
+// within the tile is loop invariant and the tile's position goes into the
+// scalar base address (no vector instructions per copy).
+template <class G>
+__device__ __forceinline__ void dma_block_full(const u16* __restrict__ src, u16* dst, int tile, int w,
+                                               int lane, int j) {
+    constexpr int D = G::D;
+    const int blk = w * G::BPW + j;
+    const int r = blk * G::RPB + lane / G::CPR;
+    const int c = (lane % G::CPR) ^ chunk_swizzle<D>(r);
+    copy_to_lds16(src + (int64_t)tile * G::BC * D, (unsigned)((r * D + c * 8) * 2), dst + blk * 512);
+}
+
 template <class G>
 __device__ __forceinline__ void dma_tile(const u16* __restrict__ src, u16* dst, int tile, int N,
                                          int w, int lane) {
@@ -673,8 +686,21 @@ __global__ void __launch_bounds__(64 * NWV, 1) attn_fwd_units_kernel(AttnArgs ar
     // the wave's 2 * BPW goes with unit 4 i / (2 BPW)): issued together after
     // the barrier, the copies of all waves queued behind each other and held
     // the waves' first MFMAs back.
+    // Tiles below TF lie wholly below N (all but a ragged last tile) and take
+    // the unclamped copy.
+    const int TF = (T + 1) * G::BC <= N ? T + 1 : T;
     auto issue_part = [&](int t, int u) __attribute__((always_inline)) {
-        if (t <= T) {
+        if (__builtin_expect(t < TF, 1)) {
+            const int s_ = (t - kt0) % NST;
+#pragma unroll
+            for (int i = 0; i < 2 * BPW; ++i) {
+                if ((4 * i) / (2 * BPW) != u) continue;
+                if (i < BPW)
+                    dma_block_full<G>(k, k_stage(s_), t, w, lane, i);
+                else
+                    dma_block_full<G>(v, v_stage(s_), t, w, lane, i - BPW);
+            }
+        } else if (t <= T) {
             const int s_ = (t - kt0) % NST;
 #pragma unroll
             for (int i = 0; i < 2 * BPW; ++i) {
