@@ -178,6 +178,32 @@ def test_wide_shapes_match_oracle(shape, causal, dtype):
     check(name, o, lse, o_ref, lse_ref, dtype)
 
 
+# Causal grids of the 4-wave kernel (128-row workgroups, two per CU) that are
+# resident in one round and larger than the CU count: 256 < B*H*ceil(N/128)
+# <= 512 with B*H*ceil(N/256) < 512.  Their order is folded (the second half
+# of the grid shortest first); an odd number of query tiles splits unevenly.
+FOLDED = [
+    # (B, H, N, D)
+    (1, 40, 1152, 128),     # 9 query tiles (odd), 360 workgroups
+    (2, 12, 1500, 64),      # 12 query tiles, ragged last tile, 288 workgroups
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", FOLDED, ids=lambda s: "B%dH%dN%dD%d" % s)
+def test_folded_one_round_grid_matches_oracle(shape, dtype):
+    B, H, N, D = shape
+    wgs = B * H * ((N + 127) // 128)
+    assert 256 < wgs <= 512 and B * H * ((N + 255) // 256) < 512
+    seed = 3000 + N + D
+    q, k, v = workloads.attn_inputs(B, H, N, D, dtype, seed, sigma_qk=1.5)
+    name = "folded grid attn causal %s B%d H%d N%d D%d seed %d" % (dtype, B, H, N, D, seed)
+    print("running", name, flush=True)
+    o, lse = run_gpu(q, k, v, True, dtype)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, True)
+    check(name, o, lse, o_ref, lse_ref, dtype)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [True, False])
 def test_wide_ramped_logits(causal, dtype):
