@@ -96,8 +96,8 @@ def extra_configs(dev):
     import workloads
     out = {}
     stream = torch.cuda.current_stream()
-    for name in ("C1", "C2", "C3", "C5"):
-        w = workloads.ATTN[name]
+    for name in ("C1", "C2", "C3", "C5", "F1K", "F2K", "F4K"):
+        w = workloads.ATTN[name] if name in workloads.ATTN else workloads.SWEEP[name]
         q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
         o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)

@@ -83,6 +83,14 @@ ATTN = {
     "C5": AttnWorkload("C5", 4, 32, 4095, 64, False, "bf16", 1.0, 1.0, 47),
 }
 
+# The rest of the FA page's sequence-length sweep (section 8: B=1, H=32,
+# D=128, causal, fp16, N = 512 ... 8192); N = 512 and 8192 are C2 and C4.
+SWEEP = {
+    "F1K": AttnWorkload("F1K", 1, 32, 1024, 128, True, "f16", 1.0, 1.0, 53),
+    "F2K": AttnWorkload("F2K", 1, 32, 2048, 128, True, "f16", 1.0, 1.0, 54),
+    "F4K": AttnWorkload("F4K", 1, 32, 4096, 128, True, "f16", 1.0, 1.0, 55),
+}
+
 # Grouped-query attention: 32 query heads sharing 8 K/V heads at D=128 (the
 # head configuration of the KV-cache page's decode measurements, section 3),
 # at the FA page's longest prefill length.
