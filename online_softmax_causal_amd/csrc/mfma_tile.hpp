@@ -24,13 +24,17 @@ template <bool BF16>
 struct Mma;
 
 // kSumRounded: whether the row sum l is taken over the 16-bit P fed to the
-// P V product (fp16: rounding error <= 2^-11 relative, so numerator and
-// denominator stay consistent and the LSE error stays below 5e-4) or over the
-// FP32 P before rounding (bf16: its 2^-9 rounding would move the LSE by up to
-// 2e-3 on rows dominated by one key).
+// P V product (with v_dot2 on the packed pairs) or over the FP32 P before
+// rounding (with FP32 adds).  Both dtypes take the FP32 sum: on gfx950 every
+// v_dot2_f32_{f16,bf16} holds the matrix pipe for about 17 cycles, so the dot2
+// form costs a sixth of an MFMA per pair, while FP32 adds issue beside the
+// MFMAs for free.  The FP32 sum is exact up to FP32 rounding, so the LSE
+// carries no P rounding error; O = sum(p~ v) / sum(p) then differs from the
+// rounded-P ratio by at most the P rounding (2^-11 fp16, 2^-9 bf16) times
+// max|v|, well inside the output tolerance.
 template <>
 struct Mma<false> {
-    static constexpr bool kSumRounded = true;
+    static constexpr bool kSumRounded = false;
     __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
