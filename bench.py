@@ -339,8 +339,9 @@ def _per_dispatch(rows, counter, match):
 
 
 def is_fwd_kernel(name: str) -> bool:
-    """The attention forward kernels (8-wave unit kernel, 4-wave ring kernel)."""
-    return "attn_fwd_units_kernel" in name or "attn_fwd_kernel" in name
+    """The attention forward kernels (8-wave pipeline kernel at D = 128, 8-wave unit kernel at
+    D = 64, 4-wave ring kernel)."""
+    return "attn_fwd_pipe_kernel" in name or "attn_fwd_units_kernel" in name or "attn_fwd_kernel" in name
 
 
 def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
@@ -363,7 +364,7 @@ def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
     a_written = mean(a_write) * 1024.0 * w_scale
     compulsory = 3 * w.B * w.H * w.N * w.D * 2 + w.B * w.H * w.N * (w.D + 1) * 4
     text = "\n".join([
-        "attn_fwd_units_kernel, causal fp16 B1 H32 N8192 D128: HBM traffic per launch (rocprofv3 --pmc)",
+        "attn_fwd_pipe_kernel, causal fp16 B1 H32 N8192 D128: HBM traffic per launch (rocprofv3 --pmc)",
         "",
         "commands (from the repository root, TMPDIR=/tmp):",
         "  " + cmd_fetch,
@@ -401,7 +402,7 @@ def summarize_sq(dirs, out_path, cmds):
                 vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     med = {k: statistics.median(v) for k, v in vals.items()}
     simds, xcds = 256 * 4, 8
-    lines = ["attn_fwd_units_kernel, causal fp16 B1 H32 N8192 D128: SQ counters per dispatch (rocprofv3 --pmc)",
+    lines = ["attn_fwd_pipe_kernel, causal fp16 B1 H32 N8192 D128: SQ counters per dispatch (rocprofv3 --pmc)",
              "", "commands (from the repository root, TMPDIR=/tmp):"]
     lines += ["  " + c for c in cmds]
     lines += ["", "counter | per dispatch (3 dispatches) | median"]
@@ -609,7 +610,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
-                     "kernel": "attn_fwd_units_kernel<f16, D=128, causal>",
+                     "kernel": "attn_fwd_pipe_kernel<f16, D=128, causal>",
                      "kernel_source_sha256_16": kernel_source_hash()},
     }
     if not args.no_cpu:

@@ -40,6 +40,7 @@
 
 #include <cstdint>
 #include <type_traits>
+#include <utility>
 
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
@@ -47,6 +48,18 @@
 
 namespace osc {
 namespace {
+
+// Compile-time loop: f(integral_constant<int, i>) for i = 0 .. N-1, always
+// fully unrolled (a #pragma unroll loop over a large body may be left rolled,
+// which turns register arrays into scratch memory).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Compile-time geometry of one kernel instance.
 //
@@ -986,6 +999,502 @@ __global__ void __launch_bounds__(64 * NWV, 1) attn_fwd_units_kernel(AttnArgs ar
     store_rows<D, QB>(st, args, seg, bh, row0, col, g);
 }
 
+// ---------------------------------------------------------------------------
+// Tile-lagged pipeline kernel: 8 waves of 32 query rows (256 rows per
+// workgroup, one workgroup per CU), two waves per SIMD.
+//
+// Iteration i of a wave issues, one after the other, the MFMAs of QK (S^T =
+// K Q^T) for key half 1 of tile i and key half 0 of tile i+1, alternating
+// with those of PV(i-1) (O^T += V^T P^T of the tile before), and hosts under
+// them the softmax of tile i, key half 0 in the first half of the iteration
+// and key half 1 in the second:
+// per MFMA one score's fma and exp (two at D = 64), the FP32 sum of the
+// exponentials and every other value one 16-bit pack.  P(i) is complete at
+// the end of iteration i and first read by PV(i) in iteration i+1, so no MFMA
+// ever waits on the exponentials, and the check that accepts P(i) (below)
+// runs once per tile, at the iteration end, before the barrier.  Each key
+// half's scores are consumed before the next tile's scores of that half are
+// written, so one buffer of scores suffices.  (FA page,
+// section 4: the recurrence is unchanged; only the order in which its steps
+// of different tiles interleave is.)
+//
+// Reference max and bound.  The first tile's scores set the reference max m
+// of each query (its exact maximum).  Every later tile's exponentials are
+// taken against the current m; if a lane's sum over the tile exceeds 2^8
+// (so some P might exceed it) or is NaN, each query whose two lanes include
+// such a lane moves m to max(m, tile max), rescales o and l, and takes the
+// tile's exponentials again (half 0's scores, overwritten by then, are
+// recomputed from K of the tile, still in LDS).  A query's decision depends only on its own
+// scores.  Between moves every P is at most 2^8, exact in fp16 and bf16
+// range, and numerator and denominator share m, so O = o / l is unchanged.
+//
+// LDS holds four K stages then four V stages.  Iteration i reads K(i),
+// K(i+1) and V(i-1) and copies K(i+3) and V(i+2) (direct global -> LDS
+// copies, issued early in the iteration); the barrier that ends iteration i
+// certifies the copies issued in iteration i-1, i.e. the data iteration i+2
+// reads first, so the operand ring runs across iteration boundaries and the
+// next iteration's first fragments are read before the barrier.  Tile t's K and V use stage
+// (t - kt0) mod 4; the loop is unrolled by four so every LDS address is a
+// per-lane base plus an immediate.
+//
+// Causal masking (and the ragged key tail) is applied in place to S(i), key
+// half 0 at the start of iteration i and key half 1 once its QK is done, only
+// for tiles that need it: the four diagonal tiles
+// of the workgroup and a ragged last tile.  A tile wholly above a wave's rows
+// is fully masked (P = 0) and still computed, while the other waves of the
+// workgroup work on it.
+template <bool BF16, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1) attn_fwd_pipe_kernel(AttnArgs args) {
+    constexpr int QB = 1;             // 32-row blocks per wave
+    constexpr int NW = 8;             // waves per workgroup
+    using G = Geo<D, NW, 4, 2, NW>;
+    using M = Mma<BF16>;
+    constexpr int KS = G::KS;         // K fragments per key half
+    constexpr int MT = G::MT;         // 32-row d blocks of O^T
+    constexpr int NQK = 2 * KS;       // K fragments per tile
+    constexpr int NPV = 4 * MT;       // V fragments per tile
+    static_assert(NQK == NPV, "QK and PV take the same number of fragments");
+    constexpr int NSTEP = NQK + NPV;  // fragments per iteration (each feeds QB MFMAs)
+    constexpr int NVAL = 32 * QB;     // scores per lane per tile
+    constexpr int VPS = NVAL / NSTEP; // hosted values per fragment step
+    constexpr int TILE = G::TILE;
+    constexpr int BPW = G::BPW;       // 1 KiB copies per wave per K (or V) tile
+    constexpr int NST = 4;            // stages of K and of V
+    constexpr int RING = 4;           // operand fragments in flight
+    constexpr int RW = 256;           // query rows per workgroup
+    constexpr float kBound = 256.0f;  // a lane's tile sum at most 2^8 keeps every P at most 2^8
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((address_space(3))) u16 lds_u16;
+    __shared__ __attribute__((aligned(1024))) u16 lds[2 * NST * TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Waves w and w + 4 share a SIMD and take adjacent 32-row blocks.
+    const int block0 = 2 * (w & 3) + (w >> 2);
+
+    const int N = args.N;
+    const float scale_log2 = args.scale_log2;
+    // Work item: longest causal query tiles first; the heads of one query
+    // tile are dealt to the 8 XCDs so each XCD keeps a fixed set of heads
+    // (and of shared K/V heads) in its L2.
+    const int bid = blockIdx.x;
+    const int per_tile = args.BH * args.nseg;
+    const int tt = bid / per_tile;
+    const int t_q = CAUSAL ? (args.T - 1 - tt) : tt;
+    const int seg = (bid - tt * per_tile) / args.BH;
+    const int jh = bid % args.BH;
+    const int bh = (args.BH & 7) ? jh : (jh & 7) * (args.BH >> 3) + (jh >> 3);
+    const int kvh = (bh / args.H) * args.Hkv + (bh % args.H) / (args.H / args.Hkv);
+    const u16* __restrict__ q = args.q + (int64_t)bh * N * D;
+    const u16* __restrict__ k = args.k + (int64_t)kvh * N * D;
+    const u16* __restrict__ v = args.v + (int64_t)kvh * N * D;
+
+    const int row_base = t_q * RW;
+    int row0[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) row0[b] = row_base + 32 * (block0 + b);
+    const int kt0 = seg * args.seg_tiles;
+    const int kv_end = min(CAUSAL ? min(row_base + RW, N) : N, (kt0 + args.seg_tiles) * G::BC);
+    const int ntiles = (kv_end + G::BC - 1) / G::BC;
+    if (kt0 >= ntiles) return;
+    const int T = ntiles - 1;   // last key tile
+    // Tiles from first_masked on need the causal mask (keys past the
+    // workgroup's first row); a tile reaching past N needs the tail mask.
+    const int first_masked = CAUSAL ? row_base / G::BC : T + 1;
+
+    WaveState<D, QB> st;
+    const int col = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const int row = row0[b] + col;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            st.qf[b][ks] = row < N ? *reinterpret_cast<const u32x4*>(q + (int64_t)row * D + ks * 16 + 8 * g)
+                                   : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) st.acc[b][mt] = f32x16{};
+        st.l[b] = 0.0f;
+    }
+
+    // Per-lane LDS fragment bases of stage 0 (pinned so that every fragment
+    // address stays a base plus an immediate offset).
+    const FragOffsets<D> fo = frag_offsets<G>(lane);
+    const lds_u32x4* kp[KS];
+    const lds_s16x4* vp[MT][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        kp[ks] = (const lds_u32x4*)((const lds_u16*)lds + fo.k[ks]);
+        asm volatile("" : "+v"(kp[ks]));
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            vp[mt][r] = (const lds_s16x4*)((const lds_u16*)lds + NST * TILE + fo.v[mt][r]);
+            asm volatile("" : "+v"(vp[mt][r]));
+        }
+    auto k_stage = [&](int s_) __attribute__((always_inline)) { return lds + s_ * TILE; };
+    auto v_stage = [&](int s_) __attribute__((always_inline)) { return lds + (NST + s_) * TILE; };
+    // K fragment (key half h, d step ks) and V^T fragment (16-key group kg,
+    // d block mt) of the tiles in stages sk and sv.
+    auto kfrag = [&](int sk, int h, int ks) __attribute__((always_inline)) {
+        return kp[ks][(sk * TILE + h * 32 * D) / 8];
+    };
+    auto vfrag = [&](int sv, int kg, int mt) __attribute__((always_inline)) {
+        const int o = (sv * TILE + kg * 16 * D) / 4;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp[mt][0] + o));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp[mt][1] + o));
+        const auto lo = __builtin_bit_cast(unsigned long long, x0);
+        const auto hi = __builtin_bit_cast(unsigned long long, x1);
+        return u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi, (unsigned)(hi >> 32)};
+    };
+    // Element e of the operand stream of an iteration of phase PH (tile i
+    // with (i - kt0) mod 4 = PH): even e the K fragments, first those of key
+    // half 1 of tile i, then those of key half 0 of tile i+1 (d step order);
+    // odd e the V^T fragments of tile i-1 in PV order (key group, d block).
+    auto frag = [&](int PH, int e) __attribute__((always_inline)) {
+        const int n = e >> 1;
+        if ((e & 1) == 0) return n < KS ? kfrag(PH, 1, n) : kfrag((PH + 1) % NST, 0, n - KS);
+        return vfrag((PH + 3) % NST, n / MT, n % MT);
+    };
+    // Copy part c (of 2 BPW) of the copies of iteration i (phase PH): K(i+3)
+    // into stage PH+3 and V(i+2) into stage PH+2.  A tile wholly below N takes
+    // the unclamped copy.
+    auto copy_part = [&](int PH, int i, int c) __attribute__((always_inline)) {
+        if (c < BPW) {
+            const int t = i + 3;
+            if (t <= T) {
+                if ((t + 1) * G::BC <= N)
+                    dma_block_full<G>(k, k_stage((PH + 3) % NST), t, w, lane, c);
+                else
+                    dma_block<G>(k, k_stage((PH + 3) % NST), t, N, w, lane, c);
+            }
+        } else {
+            const int t = i + 2;
+            if (t <= T) {
+                if ((t + 1) * G::BC <= N)
+                    dma_block_full<G>(v, v_stage((PH + 2) % NST), t, w, lane, c - BPW);
+                else
+                    dma_block<G>(v, v_stage((PH + 2) % NST), t, N, w, lane, c - BPW);
+            }
+        }
+    };
+
+    // S^T += K Q^T (first: S^T = K Q^T) and O^T += V^T P^T.
+    auto mm_qk = [&](f32x16& d, const u32x4& a, const u32x4& bq, auto first_c) __attribute__((always_inline)) {
+        d = M::run(a, bq, decltype(first_c)::value ? f32x16{} : d);
+    };
+    auto mm_pv = [&](f32x16& acc, const u32x4& a, const u32x4& bp) __attribute__((always_inline)) {
+        acc = M::run(a, bp, acc);
+    };
+
+    f32x16 s[QB][2];       // S^T: [row block][key half]
+    u32x4 pf[2][QB][4];    // 16-bit P^T: [buffer][row block][16-key group]
+    float x[NVAL], p[NVAL];
+    float r0[QB], r1[QB];  // the lane's tile sum per row block (even / odd values)
+    u32x4 ring[RING];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        r0[b] = 0.0f;
+        r1[b] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pf[0][b][j] = u32x4{0u, 0u, 0u, 0u};
+            pf[1][b][j] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // Scores of keys after the query (causal) or past N set to -inf, in key
+    // half h of tile i (sc: that half's scores of each row block).  Lane
+    // (col, g) holds keys 8(j/4) + 4g + j%4 of the half for query
+    // row0[b] + col.
+    auto mask_half = [&](f32x16 (&sc)[QB], int i, int h) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            const int key0 = i * G::BC + 32 * h;
+            const int lim = min(CAUSAL ? row0[b] + col - key0 : (1 << 30), N - 1 - key0) - 4 * g;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int c = 8 * (j >> 2) + (j & 3);
+                sc[b][j] = c > lim ? -INFINITY : sc[b][j];
+            }
+        }
+    };
+    auto mask_s = [&](int i, int h) __attribute__((always_inline)) {
+        f32x16 t[QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) t[b] = s[b][h];
+        mask_half(t, i, h);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) s[b][h] = t[b];
+    };
+    auto needs_mask = [&](int i) __attribute__((always_inline)) {
+        return i >= first_masked || (i + 1) * G::BC > N;
+    };
+
+    // Hosted work of step `step` of an iteration whose scores are in buffer
+    // sb and whose P goes to buffer sb: value vv (key half vv / (16 QB), row
+    // block (vv / 16) % QB, element vv % 16) has its fma at step vv / VPS,
+    // its exp one step later, its sum and (odd vv, with vv - 1) its pack one
+    // step after that.  The empty asm statements anchor each result where it
+    // is computed, so the work stays spread over the MFMA stream.
+    auto host_step = [&](auto sb_c, auto step_c) __attribute__((always_inline)) {
+        constexpr int sb = decltype(sb_c)::value;
+        constexpr int step = decltype(step_c)::value;
+        static_for<NVAL>([&](auto vv_c) __attribute__((always_inline)) {
+            constexpr int vv = decltype(vv_c)::value;
+            constexpr int s0 = vv / VPS;
+            constexpr int h = vv / (16 * QB), b = (vv / 16) % QB, j = vv & 15;
+            if constexpr (step == s0 + 2) {
+                if constexpr (vv & 1)
+                    r1[b] += p[vv];
+                else
+                    r0[b] += p[vv];
+                asm volatile("" ::"v"(r0[b]), "v"(r1[b]));
+                if constexpr (vv & 1) {
+                    constexpr int kg = 2 * h + (j >> 3), d = (j & 7) >> 1;
+                    pf[sb][b][kg][d] = M::pack(p[vv - 1], p[vv]);
+                    asm volatile("" ::"v"(pf[sb][b][kg][d]));
+                }
+            }
+            if constexpr (step == s0 + 1) {
+                p[vv] = fast_exp2(x[vv]);
+                asm volatile("" ::"v"(p[vv]));
+            }
+            if constexpr (step == s0) {
+                x[vv] = fmaf(s[b][h][j], scale_log2, -st.m[b]);
+                asm volatile("" ::"v"(x[vv]));
+            }
+        });
+    };
+
+    // End of the softmax of tile i (phase PH; P in buffer sb): the bound
+    // check, the rare move of the reference max, and the tile's sum into l.
+    // The move recomputes key half 0's scores (their registers hold tile
+    // i+1's by now) from K(i), still in stage PH.
+    auto settle = [&](int sb, int PH, int i) __attribute__((always_inline)) {
+        float ts[QB];
+        bool bad = false;
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            ts[b] = r0[b] + r1[b];
+            r0[b] = 0.0f;
+            r1[b] = 0.0f;
+            bad = bad || !(ts[b] <= kBound);
+        }
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+            f32x16 s0[QB];
+            static_for<KS>([&](auto ks_c) __attribute__((always_inline)) {
+                constexpr int ks = decltype(ks_c)::value;
+                const u32x4 a = kfrag(PH, 0, ks);
+#pragma unroll
+                for (int b = 0; b < QB; ++b) mm_qk(s0[b], a, st.qf[b][ks], std::bool_constant<ks == 0>{});
+            });
+            if (needs_mask(i)) mask_half(s0, i, 0);
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                // Both lanes of a query take the same decision; the exchanges
+                // run in every lane (under a partial EXEC mask they would read
+                // stale values).
+                const float ts_pair = swap32_f32(ts[b]);
+                const bool need = !(ts[b] <= kBound && ts_pair <= kBound);
+                float hm = s0[b][0];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) hm = fmaxf(hm, fmaxf(s0[b][j], s[b][1][j]));
+                hm = fmaxf(hm, swap32_f32(hm)) * scale_log2;
+                const float m_new = need ? fmaxf(st.m[b], hm) : st.m[b];
+                const float alpha = need ? fast_exp2(st.m[b] - m_new) : 1.0f;
+                st.l[b] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) st.acc[b][mt] *= alpha;
+                st.m[b] = m_new;
+                float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int j = 0; j < 16; j += 2) {
+                        const float v0 = h == 0 ? s0[b][j] : s[b][1][j];
+                        const float v1 = h == 0 ? s0[b][j + 1] : s[b][1][j + 1];
+                        const float e0 = fast_exp2(fmaf(v0, scale_log2, -m_new));
+                        const float e1 = fast_exp2(fmaf(v1, scale_log2, -m_new));
+                        a0 += e0;
+                        a1 += e1;
+                        pf[sb][b][2 * h + (j >> 3)][(j & 7) >> 1] = M::pack(e0, e1);
+                    }
+                ts[b] = a0 + a1;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < QB; ++b) st.l[b] += ts[b];
+    };
+
+    // One iteration of phase PH for tile i: QK of key half 1 of tile i and of
+    // key half 0 of tile i+1 if HQ, PV(i-1) if HP, the softmax of tile i if
+    // HOST.  On entry ring holds stream elements 0 .. RING-1; on exit it holds
+    // those of the next iteration (phase PH+1).
+    auto iteration = [&](auto ph_c, auto hq_c, auto hp_c, auto host_c, int i) __attribute__((always_inline)) {
+        constexpr int PH = decltype(ph_c)::value;
+        constexpr bool HQ = decltype(hq_c)::value;
+        constexpr bool HP = decltype(hp_c)::value;
+        constexpr bool HOST = decltype(host_c)::value;
+        constexpr int SB = PH & 1;       // buffer of tile i's P
+        constexpr int SN = SB ^ 1;       // buffer of tile i-1's P
+        const bool masked = HOST && needs_mask(i);
+        if (masked) {
+            mask_s(i, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NSTEP>([&](auto e_c) __attribute__((always_inline)) {
+            constexpr int e = decltype(e_c)::value;
+            constexpr int n = e >> 1;
+            const u32x4 a = ring[e % RING];
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                if constexpr ((e & 1) == 0) {
+                    if constexpr (HQ) {
+                        // n < KS: key half 1 of tile i; else key half 0 of tile i+1
+                        constexpr int h = n < KS ? 1 : 0, ks = n % KS;
+                        mm_qk(s[b][h], a, st.qf[b][ks], std::bool_constant<ks == 0>{});
+                    }
+                } else {
+                    if constexpr (HP) {
+                        constexpr int kg = n / MT, mt = n % MT;
+                        mm_pv(st.acc[b][mt], a, pf[SN][b][kg]);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (e == NSTEP / 2 - 1) {
+                // Key half 1 of tile i is complete: mask it before its softmax.
+                if (masked) {
+                            mask_s(i, 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (e + RING < NSTEP) ring[e % RING] = frag(PH, e + RING);
+            if constexpr (HOST) {
+                static_for<2 * BPW>([&](auto c_c) __attribute__((always_inline)) {
+                    constexpr int c = decltype(c_c)::value;
+                    if constexpr (e == 1 + 2 * c) copy_part(PH, i, c);
+                });
+                host_step(std::integral_constant<int, SB>{}, e_c);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr (HOST) {
+            host_step(std::integral_constant<int, SB>{}, std::integral_constant<int, NSTEP>{});
+            // The next iteration's first fragments: certified by the barrier
+            // that ended the previous iteration.
+#pragma unroll
+            for (int e = 0; e < RING; ++e) ring[e] = frag((PH + 1) % NST, e);
+            host_step(std::integral_constant<int, SB>{}, std::integral_constant<int, NSTEP + 1>{});
+            settle(SB, PH, i);
+            // Copies issued in this iteration may stay in flight; everything
+            // older (the data the iteration after next reads) has landed.
+            if (i + 3 <= T)
+                wait_vmcnt<2 * BPW>();
+            else if (i + 2 <= T)
+                wait_vmcnt<BPW>();
+            else
+                wait_vmcnt<0>();
+            __syncthreads();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Prologue: Q, and the copies iterations kt0-3 .. kt0-1 would have
+    // issued (K of tiles kt0 .. kt0+2, V of tiles kt0, kt0+1).
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        if (kt0 + t <= T) {
+#pragma unroll
+            for (int c = 0; c < BPW; ++c) {
+                if ((kt0 + t + 1) * G::BC <= N)
+                    dma_block_full<G>(k, k_stage(t), kt0 + t, w, lane, c);
+                else
+                    dma_block<G>(k, k_stage(t), kt0 + t, N, w, lane, c);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (kt0 + t <= T) {
+#pragma unroll
+            for (int c = 0; c < BPW; ++c) {
+                if ((kt0 + t + 1) * G::BC <= N)
+                    dma_block_full<G>(v, v_stage(t), kt0 + t, w, lane, c);
+                else
+                    dma_block<G>(v, v_stage(t), kt0 + t, N, w, lane, c);
+            }
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    // S(kt0) and the reference max from its exact row maximum.
+    {
+        u32x4 fr[NQK];
+#pragma unroll
+        for (int n = 0; n < NQK; ++n) fr[n] = kfrag(0, n / KS, n % KS);
+        static_for<NQK>([&](auto n_c) __attribute__((always_inline)) {
+            constexpr int n = decltype(n_c)::value;
+            constexpr int h = n / KS, ks = n % KS;
+#pragma unroll
+            for (int b = 0; b < QB; ++b) mm_qk(s[b][h], fr[n], st.qf[b][ks], std::bool_constant<ks == 0>{});
+        });
+    }
+    if (needs_mask(kt0)) {
+        mask_s(kt0, 0);
+        mask_s(kt0, 1);
+    }
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        float hm = s[b][0][0];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) hm = fmaxf(hm, s[b][h][j]);
+        st.m[b] = fmaxf(hm, swap32_f32(hm)) * scale_log2;
+    }
+#pragma unroll
+    for (int e = 0; e < RING; ++e) ring[e] = frag(0, e);
+
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    using Y = std::true_type;
+    using F = std::false_type;
+    // Iteration kt0 has no PV.  (It computes key half 1 of tile kt0 again
+    // and masks it again, which changes nothing.)
+    iteration(P0{}, Y{}, F{}, Y{}, kt0);
+    // Iterations kt0+1 .. T: QK of key half 0 of tile T+1 (in the last one)
+    // reads a stage holding no valid tile and its result is never used.
+    const int nmid = T - kt0;
+    const int nq = nmid / 4;
+    int i = kt0 + 1;
+    for (int qq = 0; qq < nq; ++qq, i += 4) {
+        iteration(P1{}, Y{}, Y{}, Y{}, i);
+        iteration(P2{}, Y{}, Y{}, Y{}, i + 1);
+        iteration(P3{}, Y{}, Y{}, Y{}, i + 2);
+        iteration(P0{}, Y{}, Y{}, Y{}, i + 3);
+    }
+    const int nr = nmid - 4 * nq;
+    if (nr >= 1) iteration(P1{}, Y{}, Y{}, Y{}, i++);
+    if (nr >= 2) iteration(P2{}, Y{}, Y{}, Y{}, i++);
+    if (nr >= 3) iteration(P3{}, Y{}, Y{}, Y{}, i++);
+    // PV(T): the PV half of the iteration after T.
+    switch (nr) {
+        case 0: iteration(P1{}, F{}, Y{}, F{}, i); break;
+        case 1: iteration(P2{}, F{}, Y{}, F{}, i); break;
+        case 2: iteration(P3{}, F{}, Y{}, F{}, i); break;
+        default: iteration(P0{}, F{}, Y{}, F{}, i); break;
+    }
+
+    store_rows<D, QB>(st, args, seg, bh, row0, col, g);
+}
+
 template <bool BF16, int D, bool CAUSAL, int NW, int MINWG, int STAGES, int DIST, int QB = 1>
 hipError_t launch_ring(AttnArgs a, hipStream_t stream) {
     constexpr int BR = 32 * QB * NW;
@@ -999,6 +1508,15 @@ hipError_t launch_ring(AttnArgs a, hipStream_t stream) {
     return hipLaunchKernel(
         reinterpret_cast<const void*>(&attn_fwd_kernel<BF16, D, CAUSAL, NW, MINWG, STAGES, DIST, QB>),
         dim3((unsigned)(a.T * a.BH * a.nseg)), dim3(64 * NW), params, 0, stream);
+}
+
+template <bool BF16, int D, bool CAUSAL>
+hipError_t launch_pipe(AttnArgs a, hipStream_t stream) {
+    a.T = (a.N + 255) / 256;
+    a.scale_log2 = kLog2e / __builtin_sqrtf((float)D);
+    void* params[] = {(void*)&a};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_pipe_kernel<BF16, D, CAUSAL>),
+                           dim3((unsigned)(a.T * a.BH * a.nseg)), dim3(512), params, 0, stream);
 }
 
 template <bool BF16, int D, bool CAUSAL, int QB, int NWV>
@@ -1016,13 +1534,7 @@ hipError_t launch_units(AttnArgs a, hipStream_t stream) {
 // then feeds two MFMAs.  (At D = 128 the two blocks' O accumulators, Q
 // fragments and scores exceed the 256 registers a wave has at two waves per
 // SIMD.)
-inline bool units_qb2(int64_t BH, int64_t N) {
-#ifdef OSC_QB2_MIN
-    return BH * ((N + 511) / 512) >= OSC_QB2_MIN;
-#else
-    return BH * ((N + 511) / 512) >= 512;
-#endif
-}
+inline bool units_qb2(int64_t BH, int64_t N) { return BH * ((N + 511) / 512) >= 512; }
 
 // 8 waves: the key-half unit kernel (256 query rows, one workgroup per CU).
 // 4 waves: the ring kernel, two workgroups per CU (LDS for two: copies one
@@ -1037,12 +1549,10 @@ hipError_t launch_cfg(const AttnArgs& a, int waves, hipStream_t stream) {
     }
     if constexpr (D == 64) {
         if (a.nseg == 1 && units_qb2(a.BH, a.N)) return launch_units<BF16, D, CAUSAL, 2, 8>(a, stream);
+        return launch_units<BF16, D, CAUSAL, 1, 8>(a, stream);
     } else {
-#ifdef OSC_D128_QB2W4
-        if (a.nseg == 1) return launch_units<BF16, D, CAUSAL, 2, 4>(a, stream);
-#endif
+        return launch_pipe<BF16, D, CAUSAL>(a, stream);
     }
-    return launch_units<BF16, D, CAUSAL, 1, 8>(a, stream);
 }
 
 }  // namespace

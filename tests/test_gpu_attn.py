@@ -152,13 +152,20 @@ def test_identical_keys_give_prefix_mean_on_gpu():
 
 
 # Shapes with B*H*ceil(N/256) >= 512 run 8-wave workgroups of 256 query rows
-# (the key-half unit kernel); the small shapes above run 4-wave workgroups.
+# (the tile-lagged pipeline kernel at D = 128, the key-half unit kernel at
+# D = 64); the small shapes above run 4-wave workgroups.  The pipeline kernel
+# runs its key tiles after the first in groups of four plus 0-3 more: the
+# shapes cover every remainder, ragged key tails and several query tiles.
 WIDE = [
     # (B, H, N, D, sigma_qk)
     (1, 512, 64, 128, 1.0),     # one 64-key tile per head
     (1, 512, 200, 64, 1.5),     # one partial query tile per head
     (2, 128, 300, 128, 3.0),    # ragged second tile; large logits
     (1, 256, 513, 64, 3.0),     # one row past a 256-row tile edge
+    (1, 256, 350, 128, 2.0),    # 6 key tiles (ragged): remainder 1
+    (1, 256, 400, 128, 1.5),    # 7 key tiles (ragged): remainder 2
+    (1, 128, 1024, 128, 1.0),   # 4 query tiles, 16 key tiles: remainder 3
+    (1, 96, 1500, 128, 1.0),    # 6 query tiles, ragged 24th key tile
 ]
 
 
@@ -204,16 +211,17 @@ def test_folded_one_round_grid_matches_oracle(shape, dtype):
     check(name, o, lse, o_ref, lse_ref, dtype)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [True, False])
-def test_wide_ramped_logits(causal, dtype):
+def test_wide_ramped_logits(causal, dtype, D):
     """Scores that rise (or fall) steeply along the keys: with q near 1 and
     k_j near slope_h * j, every key half of a rising head holds a new row
     maximum far above the previous one, so the reference maximum has to move
     for every half; falling heads never move it after the first key; flat and
     noisy heads sit in between.  Scaled logits reach several hundred."""
-    B, H, N, D = 1, 512, 256, 64
-    g = torch.Generator().manual_seed(2301)
+    B, H, N = 1, 512, 256
+    g = torch.Generator().manual_seed(2301 + D)
     slopes = torch.tensor([0.05, -0.05, 0.3, 0.0, 0.02, -0.3, 0.15, 0.01])
     slope = slopes[torch.arange(H) % len(slopes)].view(1, H, 1, 1)
     j = torch.arange(N, dtype=torch.float32).view(1, 1, N, 1)
@@ -221,7 +229,7 @@ def test_wide_ramped_logits(causal, dtype):
     q = (1.0 + 0.1 * torch.randn((B, H, N, D), generator=g)).to(td).contiguous()
     k = (slope * j + 0.5 * torch.randn((B, H, N, D), generator=g)).to(td).contiguous()
     v = torch.randn((B, H, N, D), generator=g).to(td).contiguous()
-    name = "wide ramped logits %s %s B1 H512 N256 D64" % ("causal" if causal else "full", dtype)
+    name = "wide ramped logits %s %s B1 H512 N256 D%d" % ("causal" if causal else "full", dtype, D)
     print("running", name, flush=True)
     o, lse = run_gpu(q, k, v, causal, dtype)
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal)
