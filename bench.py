@@ -17,12 +17,18 @@ One JSON line goes to stdout.  Besides the contract fields it carries:
   cpu_baseline  the FP64 oracle timed on this host's cores on a bounded
                 sample of the same workload (every s-th query row);
   parity_sample max-abs error of the GPU output on those sampled rows;
+  clock         GFX clock and socket power (amdsmi) during a ~2.5 s
+                sustained run of the same launch after the timed steps, the
+                TFLOP/s of that run, and the achieved rate as a fraction of
+                the MFMA peak at that clock;
   extra         the other configurations (C1, C2, C3, C5 attention; G1
                 grouped-query attention; S1 without and with the key split;
                 D1..D32 paged grouped-query decode at 1K..32K tokens; C4 and
                 C5 backward;
                 R1, R2 row softmax), timed as the median of 7 group means of
-                back-to-back launches (FA page, section 8 method).
+                back-to-back launches (FA page, section 8 method); C1, C2,
+                C3, C5, R1 and R2 also carry the FP64 oracle's parity on every
+                output element and its own timing beside the GPU's.
 Runs on one GPU only; --gpus above 1 exits with a message.
 """
 import argparse
@@ -90,11 +96,12 @@ def time_groups(fn, stream, groups=7, min_ms=2.0):
     return means[len(means) // 2], means[0]
 
 
-def extra_configs(dev):
+def extra_configs(dev, with_oracle=True):
     import torch
     import online_softmax_causal_amd as osc
     import workloads
     out = {}
+    oracle_cfgs = ("C1", "C2", "C3", "C5") if with_oracle else ()
     stream = torch.cuda.current_stream()
     for name in ("C1", "C2", "C3", "C5", "F1K", "F2K", "F4K"):
         w = workloads.ATTN[name] if name in workloads.ATTN else workloads.SWEEP[name]
@@ -106,6 +113,15 @@ def extra_configs(dev):
         tf = w.flops / (med * 1e-3) / 1e12
         out[name] = {"workload": w.describe(), "ms": round(med, 5), "ms_min": round(mn, 5),
                      "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+        if name in oracle_cfgs:
+            o.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            fn()
+            torch.cuda.synchronize()
+            base, parity = oracle_full(w, [t.cpu() for t in (q, k, v)],
+                                       (o.cpu().double().numpy(), lse.cpu().double().numpy()))
+            out[name]["parity"] = parity
+            out[name]["cpu_baseline"] = base
         del q, k, v, o, lse
     # Grouped-query attention (K/V heads shared by groups of query heads).
     w = workloads.GQA["G1"]
@@ -207,8 +223,123 @@ def extra_configs(dev):
         gbs = w.bytes / (med * 1e-3) / 1e9
         out[name] = {"workload": w.describe(), "ms": round(med, 5), "ms_min": round(mn, 5),
                      "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        if with_oracle:
+            y.fill_(float("nan"))
+            fn()
+            torch.cuda.synchronize()
+            base, parity = oracle_full(w, [x.cpu()], (y.cpu().double().numpy(),))
+            out[name]["parity"] = parity
+            out[name]["cpu_baseline"] = base
         del x, y
     return out
+
+
+def host_info():
+    """Host cores and CPU model (the oracle runs on at most 16 threads, the
+    CPU share a GPU of this machine is given)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"host_cores": os.cpu_count(), "affinity_cores": affinity, "cpu_model": model}
+
+
+def oracle_full(w, inputs, gpu_out):
+    """Run the FP64 oracle on a whole workload: its time, throughput and the
+    max-abs error of the GPU output on every element."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    if hasattr(w, "M"):   # row softmax
+        (x,) = inputs
+        y_ref = oracle.row_softmax(x, nthreads=threads)
+        secs = time.perf_counter() - t0
+        (y,) = gpu_out
+        parity = {"elements": int(y_ref.size), "max_abs_y": float(np.abs(y - y_ref).max())}
+        base = {"value": round(w.bytes / secs / 1e9, 4), "unit": "GB/s", "seconds": round(secs, 3)}
+    else:
+        q, k, v = inputs
+        if w.Hkv is not None:
+            o_ref, lse_ref = oracle.attn_fwd_gqa(q, k, v, w.causal, nthreads=threads)
+        else:
+            o_ref, lse_ref = oracle.attn_fwd(q, k, v, w.causal, nthreads=threads)
+        secs = time.perf_counter() - t0
+        o, lse = gpu_out
+        parity = {"rows": int(lse_ref.size), "max_abs_o": float(np.abs(o - o_ref).max()),
+                  "max_abs_lse": float(np.abs(lse - lse_ref).max())}
+        base = {"value": round(w.flops / secs / 1e12, 6), "unit": "TFLOP/s", "seconds": round(secs, 3)}
+    base.update({"cores": threads, "kind": "oracle", "sample": "whole workload"})
+    return base, parity
+
+
+def measure_clock(step, flops, seconds=2.5):
+    """Run `step` back to back for `seconds`, sampling the GFX clock and the
+    socket power with amdsmi; averages over the last 60% of the run.  Returns
+    None if amdsmi is not usable."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        amdsmi.amdsmi_get_gpu_metrics_info(handle)
+    except Exception:
+        return None
+    samples, stop = [], [False]
+
+    def sample():
+        while not stop[0]:
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))]
+                samples.append((time.perf_counter(), sum(clks) / len(clks) if clks else None,
+                                m.get("current_socket_power")))
+            except Exception:
+                pass
+            time.sleep(0.05)
+
+    th = threading.Thread(target=sample)
+    th.start()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step()
+        n += 20
+        torch.cuda.synchronize()
+    e1.record()
+    e1.synchronize()
+    stop[0] = True
+    th.join()
+    ms = e0.elapsed_time(e1) / n
+    late = [x for x in samples if x[0] > t0 + 0.4 * seconds and x[1] is not None]
+    if not late:
+        return None
+    mhz = sum(x[1] for x in late) / len(late)
+    watts = [x[2] for x in late if isinstance(x[2], (int, float))]
+    tflops = flops / (ms * 1e-3) / 1e12
+    # MFMA peak at the measured clock: 256 CU x 4096 FLOP per clock.
+    peak_at_clock = 256 * 4096 * mhz * 1e6 / 1e12
+    return {"clock_mhz": round(mhz, 1), "power_w": round(sum(watts) / len(watts), 1) if watts else None,
+            "sustained_ms": round(ms, 5), "sustained_tflops": round(tflops, 2),
+            "peak_at_clock_tflops": round(peak_at_clock, 1),
+            "frac_of_peak_at_clock": round(tflops / peak_at_clock, 4),
+            "launches": n, "samples": len(late),
+            "source": "amdsmi current_gfxclks (mean over 8 XCDs) and current_socket_power"}
 
 
 def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, target_s=15.0):
@@ -248,34 +379,61 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, target_s=15.0):
               "max_abs_o": float(np.abs(o_rows - o_ref).max()),
               "max_abs_lse": float(np.abs(lse_rows - lse_ref).max())}
     base = {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", **host_info(),
             "sample": "%d of %d query rows (every %d-th flat row of %s), %.3g FLOP in %.1f s, "
                       "FP64 three-stage oracle" % (len(rows), total_rows, stride, w.describe(),
                                                    flops, secs)}
     return base, parity
 
 
-def profile_pass():
-    """The program rocprofv3 wraps for the counter passes: 3 launches of the C4
-    attention kernel, then 3 plain device copies of COPY_BYTES (torch's copy
-    kernel) whose HBM traffic is known (read COPY_BYTES, write COPY_BYTES)."""
+def _launcher(name, dev):
+    """A closure launching workload `name` (C1-C5, F*, G1 attention; R1, R2 row
+    softmax) on resident inputs, and the kernel-name test that picks its
+    dispatches out of a profile."""
     import torch
     import online_softmax_causal_amd as osc
     import workloads
-    dev = torch.device("cuda:0")
-    w = workloads.ATTN["C4"]
+    if name in workloads.SOFTMAX:
+        w = workloads.SOFTMAX[name]
+        x = workloads.softmax_inputs(w.M, w.N, seed=w.seed, last=w.last).to(dev)
+        y = torch.empty_like(x)
+        return w, (lambda: osc.row_softmax(x, y, w.M, w.N)), (lambda n: "softmax" in n)
+    w = workloads.ATTN.get(name) or workloads.SWEEP.get(name) or workloads.GQA.get(name)
     q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
     o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    hkv = w.H if w.Hkv is None else w.Hkv
+    return w, (lambda: osc.attn_fwd_gqa(q, k, v, o, lse, w.B, w.H, hkv, w.N, w.D, w.causal,
+                                        w.dtype)), is_fwd_kernel
+
+
+def profile_pass(name="C4"):
+    """The program rocprofv3 wraps for the counter passes: 3 launches of
+    workload `name`, then 3 plain device copies of COPY_BYTES (torch's copy
+    kernel) whose HBM traffic is known (read COPY_BYTES, write COPY_BYTES)."""
+    import torch
+    dev = torch.device("cuda:0")
+    _, fn, _ = _launcher(name, dev)
     for _ in range(3):
-        osc.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.D, w.causal, w.dtype)
+        fn()
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print("profile pass done", flush=True)
+    print("profile pass done:", name, flush=True)
+
+
+def profile_launches(name, launches=20):
+    """Launch workload `name` `launches` times (the rocprofv3 kernel-trace target)."""
+    import torch
+    dev = torch.device("cuda:0")
+    w, fn, _ = _launcher(name, dev)
+    for _ in range(launches):
+        fn()
+    torch.cuda.synchronize()
+    print("launches:", launches, w.describe(), flush=True)
 
 
 def profile_decode(launches=30):
@@ -344,16 +502,34 @@ def is_fwd_kernel(name: str) -> bool:
     return "attn_fwd_pipe_kernel" in name or "attn_fwd_units_kernel" in name or "attn_fwd_kernel" in name
 
 
-def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
-    """Write profiles/attn_fwd_C4_traffic.txt from two rocprofv3 --pmc runs of --profile-pass."""
+def traffic_path(name):
+    return TRAFFIC_FILE if name == "C4" else os.path.join(ROOT, "profiles", "%s_%s_traffic.txt" % (
+        "row_softmax" if name.startswith("R") else "attn_fwd", name))
+
+
+def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write, name="C4"):
+    """Write profiles/<kernel>_<name>_traffic.txt from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE) of --profile-pass <name>."""
     import workloads
-    w = workloads.ATTN["C4"]
-    is_attn = is_fwd_kernel
-    is_copy = lambda n: not is_fwd_kernel(n)
+    from types import SimpleNamespace
+    if name in workloads.SOFTMAX:
+        w = workloads.SOFTMAX[name]
+        is_k = lambda n: "softmax" in n
+        compulsory = w.bytes
+        what = "row_softmax, " + w.describe()
+        srcs = ("row_softmax.hip", "online_merge.hpp")
+    else:
+        w = workloads.ATTN.get(name) or workloads.SWEEP.get(name) or workloads.GQA.get(name)
+        is_k = is_fwd_kernel
+        hkv = w.H if w.Hkv is None else w.Hkv
+        compulsory = (w.B * w.H + 2 * w.B * hkv) * w.N * w.D * 2 + w.B * w.H * w.N * (w.D + 1) * 4
+        what = "attention forward, " + w.describe()
+        srcs = ("attn_fwd.hip", "mfma_tile.hpp", "online_merge.hpp")
+    is_copy = lambda n: not is_k(n)
     fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
-    a_fetch = _per_dispatch(fr, "FETCH_SIZE", is_attn)
+    a_fetch = _per_dispatch(fr, "FETCH_SIZE", is_k)
     c_fetch = _per_dispatch(fr, "FETCH_SIZE", is_copy)
-    a_write = _per_dispatch(wr, "WRITE_SIZE", is_attn)
+    a_write = _per_dispatch(wr, "WRITE_SIZE", is_k)
     c_write = _per_dispatch(wr, "WRITE_SIZE", is_copy)
     # steady-state launches: skip the first of each kind
     mean = lambda xs: sum(xs[1:]) / max(1, len(xs) - 1) if len(xs) > 1 else xs[0]
@@ -362,17 +538,16 @@ def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
     w_scale = COPY_BYTES / (kib_c_write * 1024.0)
     a_read = mean(a_fetch) * 1024.0 * f_scale
     a_written = mean(a_write) * 1024.0 * w_scale
-    compulsory = 3 * w.B * w.H * w.N * w.D * 2 + w.B * w.H * w.N * (w.D + 1) * 4
     text = "\n".join([
-        "attn_fwd_pipe_kernel, causal fp16 B1 H32 N8192 D128: HBM traffic per launch (rocprofv3 --pmc)",
+        "%s: HBM traffic per launch (rocprofv3 --pmc)" % what,
         "",
         "commands (from the repository root, TMPDIR=/tmp):",
         "  " + cmd_fetch,
         "  " + cmd_write,
-        "  python bench.py --summarize-traffic <fetch_dir> <write_dir>",
+        "  python bench.py --summarize-traffic <fetch_dir> <write_dir> --cfg %s" % name,
         "",
-        "attention FETCH_SIZE per dispatch (KiB): " + ", ".join("%.0f" % x for x in a_fetch),
-        "attention WRITE_SIZE per dispatch (KiB): " + ", ".join("%.0f" % x for x in a_write),
+        "kernel FETCH_SIZE per dispatch (KiB): " + ", ".join("%.0f" % x for x in a_fetch),
+        "kernel WRITE_SIZE per dispatch (KiB): " + ", ".join("%.0f" % x for x in a_write),
         "copy kernel (%d bytes read + %d written) FETCH_SIZE (KiB): %s" % (
             COPY_BYTES, COPY_BYTES, ", ".join("%.0f" % x for x in c_fetch)),
         "copy kernel WRITE_SIZE (KiB): " + ", ".join("%.0f" % x for x in c_write),
@@ -382,30 +557,35 @@ def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
         "hbm_read_bytes_per_launch: %.6g" % a_read,
         "hbm_write_bytes_per_launch: %.6g" % a_written,
         "hbm_bytes_per_launch: %.6g" % (a_read + a_written),
-        "compulsory_bytes (Q,K,V read once; O fp32 + LSE written once): %.6g" % compulsory,
-        "kernel_source_sha256_16: %s" % kernel_source_hash(),
+        "compulsory_bytes (inputs read once, outputs written once): %.6g" % compulsory,
+        "traffic / compulsory: %.3f" % ((a_read + a_written) / compulsory),
+        "kernel_source_sha256_16: %s" % kernel_source_hash(srcs),
         "",
     ])
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_path(name), "w") as f:
         f.write(text)
     print(text)
 
 
-def summarize_sq(dirs, out_path, cmds):
-    """Write profiles/attn_fwd_C4_sq_counters.txt from rocprofv3 --pmc SQ passes of --profile-pass."""
+def summarize_sq(dirs, out_path, cmds, name="C4"):
+    """Write profiles/attn_fwd_<name>_sq_counters.txt from rocprofv3 --pmc SQ
+    passes of --profile-pass <name>."""
     import statistics
-    vals = {}
+    import workloads
+    w = workloads.ATTN.get(name) or workloads.SWEEP.get(name) or workloads.GQA.get(name)
+    vals, kern = {}, set()
     for d in dirs:
         rows = _pmc_rows(d)
         for r in rows:
             if is_fwd_kernel(r["Kernel_Name"]):
                 vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                kern.add(r["Kernel_Name"].split("(")[0][:90])
     med = {k: statistics.median(v) for k, v in vals.items()}
     simds, xcds = 256 * 4, 8
-    lines = ["attn_fwd_pipe_kernel, causal fp16 B1 H32 N8192 D128: SQ counters per dispatch (rocprofv3 --pmc)",
-             "", "commands (from the repository root, TMPDIR=/tmp):"]
+    lines = ["attention forward, %s: SQ counters per dispatch (rocprofv3 --pmc)" % w.describe(),
+             "kernel: " + ", ".join(sorted(kern)), "", "commands (from the repository root, TMPDIR=/tmp):"]
     lines += ["  " + c for c in cmds]
-    lines += ["", "counter | per dispatch (3 dispatches) | median"]
+    lines += ["", "counter | per dispatch | median"]
     for k in sorted(vals):
         lines.append("%s | %s | %.5g" % (k, ", ".join("%.5g" % x for x in vals[k]), med[k]))
     if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
@@ -413,14 +593,16 @@ def summarize_sq(dirs, out_path, cmds):
         util = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cycles)
         lines += ["",
                   "GPU cycles per dispatch = GRBM_GUI_ACTIVE / 8 XCDs = %.4g" % cycles,
-                  "MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) = %.3f" % util]
+                  "MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles) = %.3f" % util,
+                  "algorithmic FLOP / MFMA busy FLOP = %.3f" % (
+                      w.flops / (med["SQ_VALU_MFMA_BUSY_CYCLES"] * 1024.0))]
     if "SQ_INSTS_MFMA" in med and "SQ_VALU_MFMA_BUSY_CYCLES" in med:
         lines.append("busy cycles per MFMA instruction = %.2f (v_mfma_f32_32x32x16: 32)"
                      % (med["SQ_VALU_MFMA_BUSY_CYCLES"] / med["SQ_INSTS_MFMA"]))
-    wave_tiles = 32 * 4 * 528 * 8   # heads x (sum over query tiles of 64-key tiles) x waves
-    for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
-        if k in med:
-            lines.append("%s per wave per 64-key tile = %.1f" % (k, med[k] / wave_tiles))
+    if med.get("SQ_INSTS_MFMA"):
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+            if k in med:
+                lines.append("%s per MFMA instruction = %.2f" % (k, med[k] / med["SQ_INSTS_MFMA"]))
     lines.append("kernel_source_sha256_16: %s" % kernel_source_hash())
     lines.append("")
     with open(out_path, "w") as f:
@@ -510,8 +692,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--profile-pass", action="store_true",
-                    help="run the fixed launch sequence the counter passes profile")
+    ap.add_argument("--no-clock", action="store_true", help="skip the sustained amdsmi clock run")
+    ap.add_argument("--profile-pass", nargs="?", const="C4", default=None, metavar="CFG",
+                    help="run the fixed launch sequence the counter passes profile (default C4)")
+    ap.add_argument("--profile-launches", metavar="CFG",
+                    help="only launch workload CFG 20 times (the kernel-trace target)")
+    ap.add_argument("--cfg", default="C4", help="workload the --summarize-* options describe")
     ap.add_argument("--profile-decode", action="store_true",
                     help="only launch the 32K-context paged decode 30 times (for rocprofv3)")
     ap.add_argument("--profile-bwd", action="store_true",
@@ -526,8 +712,9 @@ def main():
     ap.add_argument("--cmd-write", default="")
     args = ap.parse_args()
     if args.summarize_sq:
-        summarize_sq(args.summarize_sq, os.path.join(ROOT, "profiles", "attn_fwd_C4_sq_counters.txt"),
-                     args.cmd.split(" ;; "))
+        summarize_sq(args.summarize_sq,
+                     os.path.join(ROOT, "profiles", "attn_fwd_%s_sq_counters.txt" % args.cfg),
+                     args.cmd.split(" ;; "), args.cfg)
         return
     if args.summarize_sq_bwd:
         summarize_sq_bwd(args.summarize_sq_bwd,
@@ -539,10 +726,13 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
-                          args.cmd_fetch, args.cmd_write)
+                          args.cmd_fetch, args.cmd_write, args.cfg)
         return
     if args.profile_pass:
-        profile_pass()
+        profile_pass(args.profile_pass)
+        return
+    if args.profile_launches:
+        profile_launches(args.profile_launches)
         return
     if args.profile_decode:
         profile_decode()
@@ -589,6 +779,7 @@ def main():
     achieved = w.flops / (kernel_ms * 1e-3) / 1e12
     o_host = o.cpu().double().numpy()
     lse_host = lse.cpu().double().numpy()
+    clock = measure_clock(step, w.flops) if not args.no_clock else None
 
     traffic = measured_traffic()
     line = {
@@ -612,13 +803,14 @@ def main():
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
                      "kernel": "attn_fwd_pipe_kernel<f16, D=128, causal>",
                      "kernel_source_sha256_16": kernel_source_hash()},
+        "clock": clock,
     }
     if not args.no_cpu:
         base, parity = cpu_baseline(w, q, k, v, o_host, lse_host)
         line["cpu_baseline"] = base
         line["parity_sample"] = parity
     if not args.no_extra:
-        line["extra"] = extra_configs(dev)
+        line["extra"] = extra_configs(dev, with_oracle=not args.no_cpu)
     print(json.dumps(line), flush=True)
 
 

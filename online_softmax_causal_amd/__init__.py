@@ -24,8 +24,14 @@ The entry points mirror the C ABI in ``include/osc_attn.h``:
     attn_bwd_workspace(B, H, N)
     attn_status_str(status)
 
-Pointer arguments accept device tensors (``torch.Tensor``, only its address is
-used) or plain integers.  ``stream`` accepts None (PyTorch's current stream on
+Pointer arguments accept device tensors or plain integer addresses.  A tensor
+argument is checked before anything is enqueued: it must live on the same GPU
+as the first tensor of the call, be contiguous, have the dtype the entry point
+expects (q, k, v, dout and the cache in the 16-bit `dtype`; o, lse and the
+gradients FP32; block_table and lengths int32) and hold at least as many
+elements as the sizes imply; otherwise ValueError is raised.  (A CPU tensor
+would hand the kernel a host address, and a short buffer would be written past
+its end.)  An integer address is passed through unchecked.  ``stream`` accepts None (PyTorch's current stream on
 the current device), a ``torch.cuda.Stream`` or an integer handle.  A nonzero
 status raises ``AttnError``.  ``attention(q, k, v, causal)`` is a convenience
 wrapper that allocates O and LSE with PyTorch and calls ``attn_fwd``.
@@ -115,6 +121,55 @@ def _ptr(x):
     raise TypeError("expected a tensor, an int address or None, got %r" % type(x))
 
 
+def _check(where, args):
+    """Validate the tensor arguments of one call before any launch.
+
+    args: (name, value, kind, numel) with kind "h" (the 16-bit dtype of the
+    call), "f32" or "i32"; numel the element count the sizes imply.  Integer
+    addresses and None are left to the C layer.
+    """
+    import torch
+    want = {"f32": torch.float32, "i32": torch.int32}
+    dev = None
+    for name, t, kind, numel in args:
+        if t is None or isinstance(t, int):
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s: %s must be a tensor, an int address or None" % (where, name))
+        if kind == "h":
+            if t.dtype not in (torch.float16, torch.bfloat16):
+                raise ValueError("%s: %s must be float16 or bfloat16, got %s" % (where, name, t.dtype))
+        elif kind != "bytes" and t.dtype != want[kind]:
+            raise ValueError("%s: %s must be %s, got %s" % (where, name, want[kind], t.dtype))
+        if kind == "bytes":
+            have = t.numel() * t.element_size()
+            if have < numel:
+                raise ValueError("%s: %s holds %d bytes, the call needs %d" % (where, name, have, numel))
+        elif t.numel() < numel:
+            raise ValueError("%s: %s holds %d elements, the sizes need %d" % (where, name, t.numel(), numel))
+        if not t.is_contiguous():
+            raise ValueError("%s: %s must be contiguous" % (where, name))
+    for name, t, _, _ in args:
+        if t is None or isinstance(t, int):
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s: %s is on %s, not on a GPU" % (where, name, t.device))
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s: %s is on %s, other arguments on %s" % (where, name, t.device, dev))
+
+
+def _check_half_dtype(where, dtype, tensors):
+    """The 16-bit tensors of a call must match its dtype argument."""
+    import torch
+    code = _dtype(dtype)
+    td = {ATTN_F16: torch.float16, ATTN_BF16: torch.bfloat16}.get(code)
+    for name, t in tensors:
+        if isinstance(t, torch.Tensor) and td is not None and t.dtype != td:
+            raise ValueError("%s: %s is %s but dtype says %s" % (where, name, t.dtype, td))
+
+
 def _stream(s):
     if s is None:
         import torch
@@ -142,6 +197,10 @@ def attn_status_str(status: int) -> str:
 
 def attn_fwd(q, k, v, o, lse, B, H, N, D, causal, dtype, stream=None) -> None:
     """Enqueue attention forward (see include/osc_attn.h); raises AttnError on a bad status."""
+    n = int(B) * int(H) * int(N)
+    _check_half_dtype("attn_fwd", dtype, [("q", q), ("k", k), ("v", v)])
+    _check("attn_fwd", [("q", q, "h", n * int(D)), ("k", k, "h", n * int(D)), ("v", v, "h", n * int(D)),
+                        ("o", o, "f32", n * int(D)), ("lse", lse, "f32", n)])
     st = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N),
                          int(D), int(bool(causal)), _dtype(dtype), _stream(stream))
     if st != 0:
@@ -150,6 +209,11 @@ def attn_fwd(q, k, v, o, lse, B, H, N, D, causal, dtype, stream=None) -> None:
 
 def attn_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, stream=None) -> None:
     """Enqueue grouped-query attention forward (K/V have Hkv heads, Hkv divides H)."""
+    n, nk = int(B) * int(H) * int(N), int(B) * int(Hkv) * int(N)
+    _check_half_dtype("attn_fwd_gqa", dtype, [("q", q), ("k", k), ("v", v)])
+    _check("attn_fwd_gqa", [("q", q, "h", n * int(D)), ("k", k, "h", nk * int(D)),
+                            ("v", v, "h", nk * int(D)), ("o", o, "f32", n * int(D)),
+                            ("lse", lse, "f32", n)])
     st = load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                              int(Hkv), int(N), int(D), int(bool(causal)), _dtype(dtype),
                              _stream(stream))
@@ -166,6 +230,12 @@ def attn_fwd_splitkv_workspace(B, H, N, D, causal, num_splits=0) -> int:
 def attn_fwd_splitkv(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, num_splits, workspace,
                      workspace_bytes, stream=None) -> None:
     """Enqueue split-KV attention forward (partial states in `workspace`, then a merge)."""
+    n, nk = int(B) * int(H) * int(N), int(B) * int(Hkv) * int(N)
+    _check_half_dtype("attn_fwd_splitkv", dtype, [("q", q), ("k", k), ("v", v)])
+    _check("attn_fwd_splitkv", [("q", q, "h", n * int(D)), ("k", k, "h", nk * int(D)),
+                                ("v", v, "h", nk * int(D)), ("o", o, "f32", n * int(D)),
+                                ("lse", lse, "f32", n),
+                                ("workspace", workspace, "bytes", max(0, int(workspace_bytes)))])
     st = load().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                                  int(Hkv), int(N), int(D), int(bool(causal)), _dtype(dtype),
                                  int(num_splits), _ptr(workspace), int(workspace_bytes),
@@ -183,12 +253,31 @@ def paged_decode_workspace(B, Hq, Hkv, D, page_size, max_pages, num_splits=0) ->
 def paged_decode(q, cache, block_table, lengths, o, lse, B, Hq, Hkv, D, page_size, num_pages,
                  max_pages, dtype, num_splits, workspace, workspace_bytes, stream=None) -> None:
     """Enqueue one paged grouped-query decode step (block_table, lengths: int32 device)."""
+    nq = int(B) * int(Hq)
+    _check_half_dtype("paged_decode", dtype, [("q", q), ("cache", cache)])
+    _check("paged_decode", [("q", q, "h", nq * int(D)),
+                            ("cache", cache, "h", int(num_pages) * 2 * int(page_size) * int(Hkv) * int(D)),
+                            ("block_table", block_table, "i32", int(B) * int(max_pages)),
+                            ("lengths", lengths, "i32", int(B)), ("o", o, "f32", nq * int(D)),
+                            ("lse", lse, "f32", nq),
+                            ("workspace", workspace, "bytes", max(0, int(workspace_bytes)))])
     st = load().paged_decode(_ptr(q), _ptr(cache), _ptr(block_table), _ptr(lengths), _ptr(o),
                              _ptr(lse), int(B), int(Hq), int(Hkv), int(D), int(page_size),
                              int(num_pages), int(max_pages), _dtype(dtype), int(num_splits),
                              _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != 0:
         raise AttnError(st, "paged_decode")
+
+
+def _check_bwd(where, q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, dtype, workspace,
+               workspace_bytes):
+    n, nk = int(B) * int(H) * int(N), int(B) * int(Hkv) * int(N)
+    d = int(D)
+    _check_half_dtype(where, dtype, [("q", q), ("k", k), ("v", v), ("dout", dout)])
+    _check(where, [("q", q, "h", n * d), ("k", k, "h", nk * d), ("v", v, "h", nk * d),
+                   ("o", o, "f32", n * d), ("lse", lse, "f32", n), ("dout", dout, "h", n * d),
+                   ("dq", dq, "f32", n * d), ("dk", dk, "f32", nk * d), ("dv", dv, "f32", nk * d),
+                   ("workspace", workspace, "bytes", max(0, int(workspace_bytes)))])
 
 
 def attn_bwd_workspace(B, H, N) -> int:
@@ -199,6 +288,8 @@ def attn_bwd_workspace(B, H, N) -> int:
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, dtype, workspace,
              workspace_bytes, stream=None) -> None:
     """Enqueue attention backward (dq, dk, dv FP32) from the forward's o and lse."""
+    _check_bwd("attn_bwd", q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, D, dtype, workspace,
+               workspace_bytes)
     st = load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                          _ptr(dk), _ptr(dv), int(B), int(H), int(N), int(D), int(bool(causal)),
                          _dtype(dtype), _ptr(workspace), int(workspace_bytes), _stream(stream))
@@ -209,6 +300,8 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, dtype, works
 def attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, causal, dtype, workspace,
                  workspace_bytes, stream=None) -> None:
     """Enqueue attention backward with Hkv shared K/V heads (k, v, dk, dv [B, Hkv, N, D])."""
+    _check_bwd("attn_bwd_gqa", q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, dtype, workspace,
+               workspace_bytes)
     st = load().attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                              _ptr(dk), _ptr(dv), int(B), int(H), int(Hkv), int(N), int(D),
                              int(bool(causal)), _dtype(dtype), _ptr(workspace),
@@ -219,6 +312,7 @@ def attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, causal, dty
 
 def row_softmax(x, y, M, N, stream=None) -> None:
     """Enqueue the row softmax of an FP32 [M, N] matrix; raises AttnError on a bad status."""
+    _check("row_softmax", [("x", x, "f32", int(M) * int(N)), ("y", y, "f32", int(M) * int(N))])
     st = load().row_softmax(_ptr(x), _ptr(y), int(M), int(N), _stream(stream))
     if st != 0:
         raise AttnError(st, "row_softmax")
@@ -228,6 +322,8 @@ def attention(q, k, v, causal: bool, stream=None):
     """O (FP32) and LSE (FP32) for contiguous device tensors q, k, v of shape [B, H, N, D]."""
     import torch
     B, H, N, D = q.shape
+    if not q.is_cuda:
+        raise ValueError("attention: q is on %s, not on a GPU" % q.device)
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous [B, H, N, D]")
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:

@@ -288,3 +288,71 @@ def test_product_package_never_touches_the_oracle():
         if os.path.isfile(path) and path.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
             text = open(path).read()
             assert "oracle" not in text.lower(), path
+
+
+# The Python binding checks tensor arguments before anything reaches the C
+# layer: a CPU tensor would hand the kernel a host address, and a tensor too
+# small for the sizes would be written past its end.  These run without a GPU.
+
+def _f16(n):
+    import torch
+    return torch.zeros(n, dtype=torch.float16)
+
+
+def _f32(n):
+    import torch
+    return torch.zeros(n, dtype=torch.float32)
+
+
+def test_binding_rejects_cpu_tensors():
+    B, H, N, D = 1, 2, 8, 64
+    n = B * H * N * D
+    with pytest.raises(ValueError, match="not on a GPU"):
+        osc.attn_fwd(_f16(n), _f16(n), _f16(n), _f32(n), _f32(B * H * N), B, H, N, D, True, "f16", 0)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        osc.row_softmax(_f32(12), _f32(12), 3, 4, 0)
+    import torch
+    with pytest.raises(ValueError, match="not on a GPU"):
+        osc.attention(torch.zeros((B, H, N, D), dtype=torch.float16),
+                      torch.zeros((B, H, N, D), dtype=torch.float16),
+                      torch.zeros((B, H, N, D), dtype=torch.float16), True)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_binding_rejects_undersized_tensors(which):
+    B, H, N, D = 1, 2, 8, 64
+    n = B * H * N * D
+    args = {"q": _f16(n), "k": _f16(n), "v": _f16(n), "o": _f32(n), "lse": _f32(B * H * N)}
+    short = args[which]
+    args[which] = short[: short.numel() - 1]
+    with pytest.raises(ValueError, match="elements, the sizes need"):
+        osc.attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], B, H, N, D, True, "f16", 0)
+
+
+def test_binding_rejects_wrong_dtypes_and_layouts():
+    import torch
+    B, H, N, D = 1, 2, 8, 64
+    n = B * H * N * D
+    with pytest.raises(ValueError, match="must be torch.float32"):
+        osc.attn_fwd(_f16(n), _f16(n), _f16(n), _f16(n), _f32(B * H * N), B, H, N, D, True, "f16", 0)
+    with pytest.raises(ValueError, match="float16 or bfloat16|dtype says"):
+        osc.attn_fwd(_f32(n), _f16(n), _f16(n), _f32(n), _f32(B * H * N), B, H, N, D, True, "f16", 0)
+    with pytest.raises(ValueError, match="dtype says"):
+        osc.attn_fwd(torch.zeros(n, dtype=torch.bfloat16), torch.zeros(n, dtype=torch.bfloat16),
+                     torch.zeros(n, dtype=torch.bfloat16), _f32(n), _f32(B * H * N), B, H, N, D, True,
+                     "f16", 0)
+    strided = _f32(2 * n)[::2]
+    with pytest.raises(ValueError, match="contiguous"):
+        osc.attn_fwd(_f16(n), _f16(n), _f16(n), strided, _f32(B * H * N), B, H, N, D, True, "f16", 0)
+    with pytest.raises(ValueError, match="int32"):
+        osc.paged_decode(_f16(2 * 64), _f16(4 * 2 * 16 * 1 * 64), _f32(2), torch.zeros(1, dtype=torch.int32),
+                         _f32(2 * 64), _f32(2), 1, 2, 1, 64, 16, 4, 2, "f16", 0, None, 0, 0)
+    with pytest.raises(ValueError, match="bytes, the call needs"):
+        osc.attn_fwd_splitkv(_f16(n), _f16(n), _f16(n), _f32(n), _f32(B * H * N), B, H, H, N, D, True,
+                             "f16", 2, _f32(3), 16, 0)
+    for name, sz in (("dq", n - 1), ("dk", n - 1), ("dv", n - 1)):
+        g = {"dq": _f32(n), "dk": _f32(n), "dv": _f32(n)}
+        g[name] = _f32(sz)
+        with pytest.raises(ValueError, match="elements, the sizes need"):
+            osc.attn_bwd(_f16(n), _f16(n), _f16(n), _f32(n), _f32(B * H * N), _f16(n), g["dq"], g["dk"],
+                         g["dv"], B, H, N, D, True, "f16", _f32(64), 256, 0)

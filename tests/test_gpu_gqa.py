@@ -96,3 +96,30 @@ def test_gqa_g1_sampled_rows():
     rows = workloads.sample_rows(w.B, w.H, w.N, 384, seed=w.seed)
     o_ref, lse_ref = oracle.attn_rows_gqa(q, k, v, w.causal, rows)
     check("G1 sampled", o.reshape(-1, w.D)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, w.dtype)
+
+
+# Grouped heads on the 8-wave workgroups (B*H*ceil(N/256) >= 512): the small
+# shapes above all run the 4-wave ring kernel.  Ragged N; every element
+# compared.
+WIDE_GQA = [
+    # (B, H, Hkv, N, D)
+    (1, 256, 32, 500, 128),   # groups of 8, ragged second query tile
+    (2, 128, 16, 300, 64),    # groups of 8 at D = 64
+    (1, 512, 128, 200, 128),  # groups of 4, one partial query tile
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", WIDE_GQA, ids=lambda s: "B%dH%dKV%dN%dD%d" % s)
+def test_gqa_wide_shapes_match_oracle(shape, causal, dtype):
+    B, H, Hkv, N, D = shape
+    assert B * H * ((N + 255) // 256) >= 512 and Hkv < H
+    seed = 3200 + N * 5 + H * 3 + Hkv + (1 if causal else 0)
+    q, k, v = workloads.gqa_inputs(B, H, Hkv, N, D, dtype, seed, sigma_qk=1.5)
+    name = "wide gqa %s %s B%d H%d Hkv%d N%d D%d seed %d" % (
+        "causal" if causal else "full", dtype, B, H, Hkv, N, D, seed)
+    print("running", name, flush=True)
+    o, lse = run_gqa(q, k, v, causal, dtype)
+    o_ref, lse_ref = oracle.attn_fwd_gqa(q, k, v, causal)
+    check(name, o, lse, o_ref, lse_ref, dtype)
