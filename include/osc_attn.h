@@ -28,7 +28,9 @@
  * Conventions (all entry points):
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *     allocates no memory (scratch space comes from a caller's workspace
- *     argument), keeps no state between calls and never synchronises.
+ *     argument; paged_decode_noalloc uses a fixed array of the library
+ *     instead, whose device address it keeps), keeps no other state between
+ *     calls and never synchronises.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns at once.  Completion is observed with the caller's own stream or
  *     event synchronisation; a fault during execution surfaces there.
@@ -224,6 +226,36 @@ attn_status_t paged_decode(const void *q, const void *cache, const int32_t *bloc
  */
 int64_t paged_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
                                int64_t max_pages, int num_splits);
+
+/* Bytes of the fixed segment-state array of paged_decode_noalloc (32 MiB). */
+#define PAGED_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/*
+ * paged_decode_noalloc - paged_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same call without a workspace argument.  The
+ * segment states go to a fixed array of PAGED_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on every device it runs on until the process ends.
+ * The call itself allocates nothing (no hipMalloc, no hipFree); its first
+ * call on a device looks up that device's array address (hipGetSymbolAddress)
+ * with the device current and keeps it.
+ *
+ *   Arguments, layouts, errors and results as for paged_decode, which it
+ *   matches bit for bit.  The stream must belong to the current device.
+ *   paged_decode_workspace(...) above PAGED_NOALLOC_SCRATCH_BYTES:
+ *   ATTN_ERR_WORKSPACE (pass a smaller num_splits or use paged_decode).
+ *   The address lookup failing: ATTN_ERR_LAUNCH.
+ *
+ * All calls on one device share its array, and each segment's state is
+ * written before it is read, so nothing carries over from one call to the
+ * next.  Calls whose kernels may overlap on one device (different streams
+ * without ordering between them) race on the array: order them.
+ */
+attn_status_t paged_decode_noalloc(const void *q, const void *cache, const int32_t *block_table,
+                                   const int32_t *lengths, float *o, float *lse, int64_t B,
+                                   int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                                   int64_t num_pages, int64_t max_pages, attn_dtype_t dtype,
+                                   int num_splits, hipStream_t stream);
 
 /*
  * attn_bwd - gradients of the attention forward (attn_fwd) with respect to

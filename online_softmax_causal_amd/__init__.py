@@ -17,6 +17,8 @@ The entry points mirror the C ABI in ``include/osc_attn.h``:
                  num_pages, max_pages, dtype, num_splits, workspace, workspace_bytes,
                  stream=None)
     paged_decode_workspace(B, Hq, Hkv, D, page_size, max_pages, num_splits=0)
+    paged_decode_noalloc(q, cache, block_table, lengths, o, lse, B, Hq, Hkv, D, page_size,
+                         num_pages, max_pages, dtype, num_splits, stream=None)
     attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, dtype, workspace,
              workspace_bytes, stream=None)
     attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, causal, dtype,
@@ -46,6 +48,7 @@ LIB_PATH = os.path.join(_PKG, "libosc_attn.so")
 
 ATTN_F16 = 0
 ATTN_BF16 = 1
+PAGED_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # include/osc_attn.h
 STATUS = {
     0: "ATTN_OK",
     1: "ATTN_ERR_NULL",
@@ -57,8 +60,8 @@ STATUS = {
     7: "ATTN_ERR_WORKSPACE",
 }
 EXPORTS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace",
-           "paged_decode", "paged_decode_workspace", "attn_bwd", "attn_bwd_gqa", "attn_bwd_workspace",
-           "row_softmax", "attn_status_str")
+           "paged_decode", "paged_decode_workspace", "paged_decode_noalloc", "attn_bwd",
+           "attn_bwd_gqa", "attn_bwd_workspace", "row_softmax", "attn_status_str")
 
 _lib = None
 
@@ -95,6 +98,9 @@ def load():
     lib.paged_decode.restype = ctypes.c_int
     lib.paged_decode_workspace.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     lib.paged_decode_workspace.restype = i64
+    lib.paged_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                         i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.paged_decode_noalloc.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                              ctypes.c_int, vp, i64, vp]
     lib.attn_bwd.restype = ctypes.c_int
@@ -267,6 +273,25 @@ def paged_decode(q, cache, block_table, lengths, o, lse, B, Hq, Hkv, D, page_siz
                              _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != 0:
         raise AttnError(st, "paged_decode")
+
+
+def paged_decode_noalloc(q, cache, block_table, lengths, o, lse, B, Hq, Hkv, D, page_size,
+                         num_pages, max_pages, dtype, num_splits, stream=None) -> None:
+    """paged_decode without a workspace: the segment states go to the library's
+    fixed per-device array of PAGED_NOALLOC_SCRATCH_BYTES bytes."""
+    nq = int(B) * int(Hq)
+    _check_half_dtype("paged_decode_noalloc", dtype, [("q", q), ("cache", cache)])
+    _check("paged_decode_noalloc", [
+        ("q", q, "h", nq * int(D)),
+        ("cache", cache, "h", int(num_pages) * 2 * int(page_size) * int(Hkv) * int(D)),
+        ("block_table", block_table, "i32", int(B) * int(max_pages)),
+        ("lengths", lengths, "i32", int(B)), ("o", o, "f32", nq * int(D)), ("lse", lse, "f32", nq)])
+    st = load().paged_decode_noalloc(_ptr(q), _ptr(cache), _ptr(block_table), _ptr(lengths),
+                                     _ptr(o), _ptr(lse), int(B), int(Hq), int(Hkv), int(D),
+                                     int(page_size), int(num_pages), int(max_pages), _dtype(dtype),
+                                     int(num_splits), _stream(stream))
+    if st != 0:
+        raise AttnError(st, "paged_decode_noalloc")
 
 
 def _check_bwd(where, q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, dtype, workspace,

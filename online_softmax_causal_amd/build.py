@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libosc_attn.so")
-SOURCES = ["attn_fwd.hip", "bwd.hip", "decode.hip", "splitkv.hip", "row_softmax.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "bwd.hip", "decode.hip", "splitkv.hip", "row_softmax.hip", "api.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -6,6 +6,29 @@
 #include "osc_attn.h"
 #include "validate.hpp"
 
+namespace osc {
+
+// Decode split plan and segment-state bytes for valid sizes; false (with the
+// status to report) if they are not.
+bool paged_decode_plan_checked(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                               int64_t num_pages, int64_t max_pages, int num_splits,
+                               attn_status_t* status, int* log2_page, DecodePlan* plan,
+                               int64_t* bytes) {
+    if (!paged_sizes_ok(B, Hq, Hkv, D, page_size, num_pages, max_pages, status, log2_page))
+        return false;
+    *status = ATTN_ERR_SHAPE;
+    if (num_splits < 0 || num_splits > PAGED_MAX_SPLITS) return false;
+    *plan = paged_decode_plan(B, Hkv, max_pages * page_size, num_splits);
+    if (B * Hkv * plan->nseg >= (int64_t(1) << 31)) return false;
+    int64_t words = 0;
+    if (!mul_below_2_62(B * Hq * (D + 2), plan->nseg, &words) || words >= (int64_t(1) << 60))
+        return false;
+    *bytes = plan->nseg > 1 ? words * 4 : 0;
+    return true;
+}
+
+}  // namespace osc
+
 extern "C" {
 
 static attn_status_t attn_fwd_impl(const void* q, const void* k, const void* v, float* o,
@@ -112,22 +135,6 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const float*
                         workspace_bytes, stream);
 }
 
-// Decode split plan and workspace size for valid sizes; false if they are not.
-static bool paged_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
-                       int64_t num_pages, int64_t max_pages, int num_splits, attn_status_t* status,
-                       int* log2_page, osc::DecodePlan* plan, int64_t* bytes) {
-    if (!osc::paged_sizes_ok(B, Hq, Hkv, D, page_size, num_pages, max_pages, status, log2_page))
-        return false;
-    *status = ATTN_ERR_SHAPE;
-    if (num_splits < 0 || num_splits > PAGED_MAX_SPLITS) return false;
-    *plan = osc::paged_decode_plan(B, Hkv, max_pages * page_size, num_splits);
-    if (B * Hkv * plan->nseg >= (int64_t(1) << 31)) return false;
-    int64_t words = 0;
-    if (!osc::mul_below_2_62(B * Hq * (D + 2), plan->nseg, &words) || words >= (int64_t(1) << 60))
-        return false;
-    *bytes = plan->nseg > 1 ? words * 4 : 0;
-    return true;
-}
 
 int64_t paged_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
                                int64_t max_pages, int num_splits) {
@@ -136,7 +143,8 @@ int64_t paged_decode_workspace(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, in
     osc::DecodePlan plan;
     int64_t bytes = 0;
     // The cache size does not enter the plan; one page stands in for it.
-    return paged_plan(B, Hq, Hkv, D, page_size, 1, max_pages, num_splits, &st, &lp, &plan, &bytes)
+    return osc::paged_decode_plan_checked(B, Hq, Hkv, D, page_size, 1, max_pages, num_splits, &st,
+                                           &lp, &plan, &bytes)
                ? bytes
                : -1;
 }
@@ -150,8 +158,8 @@ attn_status_t paged_decode(const void* q, const void* cache, const int32_t* bloc
     int lp = 0;
     osc::DecodePlan plan;
     int64_t need = 0;
-    if (!paged_plan(B, Hq, Hkv, D, page_size, num_pages, max_pages, num_splits, &st, &lp, &plan,
-                    &need)) {
+    if (!osc::paged_decode_plan_checked(B, Hq, Hkv, D, page_size, num_pages, max_pages,
+                                        num_splits, &st, &lp, &plan, &need)) {
         // A null pointer is reported before a size problem, as for attention.
         if (!q || !cache || !block_table || !lengths || !o || !lse) return ATTN_ERR_NULL;
         return st;

@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "osc_attn.h"
+
 namespace osc {
 
 // Waves per workgroup (4 or 8) for a problem of BH heads of N rows.
@@ -61,6 +63,14 @@ struct DecodePlan {
 
 // requested = 0 chooses automatically; cap = max_pages * T.
 DecodePlan paged_decode_plan(int64_t B, int64_t Hkv, int64_t cap, int requested);
+
+// The plan of a paged decode call after checking its sizes, and the bytes of
+// segment states it needs (0 for one segment); false, with the status to
+// report, if the sizes are invalid.  Host computation only (api.hip).
+bool paged_decode_plan_checked(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                               int64_t num_pages, int64_t max_pages, int num_splits,
+                               attn_status_t* status, int* log2_page, DecodePlan* plan,
+                               int64_t* bytes);
 
 // With plan.nseg > 1, part_o [nseg, B*Hq, D] and part_ml [nseg, B*Hq] receive
 // the segments' states and the split-KV merge kernel combines them.
