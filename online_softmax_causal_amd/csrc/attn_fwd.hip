@@ -239,7 +239,7 @@ __device__ __forceinline__ void softmax_pv_tile(WaveState<G::D, QB>& st, const F
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][kb][i]);
         mx = fmaxf(mx, swap32_f32(mx));
         tile_m[b] = mx * scale_log2;
-        grow[b] = tile_m[b] > st.m[b] + kRescaleSlack;
+        grow[b] = tile_m[b] > st.m[b] + rescale_slack<BF16>();
         any_grow = any_grow || grow[b];
     }
     // Each query decides for itself (so a row's result never depends on

@@ -201,7 +201,7 @@ paged_decode_kernel(DecodeArgs a) {
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
         mx = fmaxf(mx, swap32_f32(mx));
         const float tile_m = mx * a.scale_log2;
-        const bool grow = tile_m > m + kRescaleSlack;
+        const bool grow = tile_m > m + rescale_slack<BF16>();
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             const float m_new = grow ? tile_m : m;
             const float alpha = grow ? online_rescale(m, m_new) : 1.0f;

@@ -91,6 +91,16 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
 // unchanged.  This skips the rescale of the O accumulator on most tiles.
 constexpr float kRescaleSlack = 8.0f;
 
+// The slack the kernels that take an exact tile max use.  With bf16 inputs
+// P is rounded to 8 significant bits before P V, while l sums the FP32 P, so
+// a row dominated by one key carries that key's rounding (up to 2^-8
+// relative) into O.  Moving m to every new maximum makes the largest P of
+// the row exactly 1, which rounds exactly; fp16 (2^-11) keeps the slack.
+template <bool BF16>
+constexpr float rescale_slack() {
+    return BF16 ? 0.0f : kRescaleSlack;
+}
+
 __device__ __forceinline__ u32x4 tr16_b64x2(const u16* p0, const u16* p1) {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
