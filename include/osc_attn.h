@@ -35,7 +35,12 @@
  *     returns at once.  Completion is observed with the caller's own stream or
  *     event synchronisation; a fault during execution surfaces there.
  *   - Arguments are validated before anything is enqueued.  On any error
- *     nothing is enqueued and the outputs are left untouched.
+ *     nothing is enqueued and the outputs are left untouched, with one
+ *     exception: the calls that launch several kernels in order
+ *     (attn_fwd_splitkv, paged_decode, paged_decode_noalloc, attn_bwd,
+ *     attn_bwd_gqa) return ATTN_ERR_LAUNCH if the runtime refuses a later
+ *     launch, and the kernels launched before it stay enqueued; the
+ *     workspace and the outputs are then undefined.
  *   - Tensors are dense and row-major (contiguous); the library cannot check
  *     that the buffers are as large as the sizes say.
  *   - Unsupported shapes are rejected, never answered approximately (FA page,

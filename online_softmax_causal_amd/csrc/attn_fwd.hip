@@ -33,9 +33,12 @@
 //     the hardware's round-robin dispatch over the 8 XCDs, consecutive
 //     workgroups are different heads of the same query tile, so each XCD keeps
 //     a fixed subset of heads and their K/V stays in that XCD's L2.
-// Two kernels: the key-half unit kernel (8 waves, 256 query rows per
-// workgroup, one workgroup per CU; used when there are enough workgroups of
-// 256 rows) and the ring kernel (4 waves, 128 rows, two workgroups per CU).
+// Three kernels: the tile-lagged pipeline kernel (D = 128) and the key-half
+// unit kernel (D = 64), both 8 waves and 256 query rows per workgroup (512
+// for the unit kernel with two row blocks per wave), one workgroup per CU,
+// used when there are enough workgroups of 256 rows and for every key split;
+// and the ring kernel (4 waves, 128 rows, two workgroups per CU) for grids too
+// small for those.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

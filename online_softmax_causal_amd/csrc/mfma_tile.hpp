@@ -28,10 +28,13 @@ struct Mma;
 // rounding (with FP32 adds).  Both dtypes take the FP32 sum: on gfx950 every
 // v_dot2_f32_{f16,bf16} holds the matrix pipe for about 17 cycles, so the dot2
 // form costs a sixth of an MFMA per pair, while FP32 adds issue beside the
-// MFMAs for free.  The FP32 sum is exact up to FP32 rounding, so the LSE
-// carries no P rounding error; O = sum(p~ v) / sum(p) then differs from the
-// rounded-P ratio by at most the P rounding (2^-11 fp16, 2^-9 bf16) times
-// max|v|, well inside the output tolerance.
+// MFMAs.  The FP32 sum carries no P rounding error into the LSE.  O =
+// sum(p~ v) / sum(p) then differs from the rounded-P ratio by up to the P
+// rounding (unit roundoff 2^-11 fp16, 2^-8 bf16) times max|v| when one key
+// dominates a row and its P is not exactly 1: 2.4e-3 at |v| = 5 in fp16, and
+// 2e-2 in bf16.  Kernels that take an exact tile max make the dominant P
+// exactly 1 in bf16 (rescale_slack below); the kernels with a stale
+// reference max keep this bound.
 template <>
 struct Mma<false> {
     static constexpr bool kSumRounded = false;
