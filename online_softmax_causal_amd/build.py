@@ -28,9 +28,16 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-source flags.  attn_fwd.hip: VGPR-form MFMAs, so the key-split kernel
+# (one wave per SIMD, where the compiler would otherwise give every MFMA AGPR
+# accumulators and copy the scores out) keeps its accumulators in VGPRs; the
+# file's other kernels compile to the same instructions with or without it.
+SRC_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + SRC_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed on %s:\n%s" % (src, r.stderr))
@@ -43,7 +50,8 @@ def check_m0(src: str) -> None:
     instruction uses M0, so check the generated gfx950 assembly: every M0
     reference must be one of those writes, directly followed by the copy."""
     asm = os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
-    cmd = [HIPCC] + FLAGS + ["-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", asm]
+    cmd = [HIPCC] + FLAGS + SRC_FLAGS.get(src, []) + ["-S", "--cuda-device-only",
+                                                       os.path.join(CSRC, src), "-o", asm]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc -S failed on %s:\n%s" % (src, r.stderr))

@@ -536,6 +536,178 @@ attn_fwd_kernel(AttnArgs args) {
 }
 
 // ---------------------------------------------------------------------------
+// Key-split kernel: for grids of at most one workgroup per CU, where the
+// longest workgroup's walk over its key tiles is the critical path.  NW
+// waves, one per SIMD with NW = 4: the first NW/2 take 32-row blocks and the
+// even key tiles of the workgroup, the other NW/2 the same rows and the odd
+// key tiles, each with its own (m, l, o) (the ring kernel's per-tile steps,
+// FA page section 4), so a SIMD walks half the keys.  Step j holds tiles 2j
+// and 2j+1 in one LDS stage (K and V of each; two stages, the copies of step
+// j+1 in flight during step j).  At the end each odd-tile wave hands its
+// state to its partner through LDS and the partner merges the two with the
+// split-KV law (m = max, each part rescaled to it; "CUDA KV Cache: paged
+// storage and long-context decode" (chengzipai.xyz), section 6.4) before
+// storing the rows.
+// With one wave per SIMD a wave may use 512 registers, and by default the
+// compiler then gives every MFMA AGPR accumulators and copies the scores out
+// to VGPRs for the softmax; this file is built with VGPR-form MFMAs (build.py),
+// which keeps them in VGPRs (222 registers, no copies).  The other kernels
+// of the file compile to the same instructions either way.
+template <bool BF16, int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW) attn_fwd_ksplit_kernel(AttnArgs args) {
+    constexpr int QB = 1;
+    using G = Geo<D, NW, 2, 1, NW>;
+    constexpr int TILE = G::TILE;
+    constexpr int SLOT = 2 * TILE;     // K then V of one tile
+    constexpr int STAGE = 2 * SLOT;    // the two tiles of one step
+    constexpr int NB = NW / 2;         // 32-row blocks
+    constexpr int BR = 32 * NB;        // query rows per workgroup
+    constexpr int MT = G::MT;
+    __shared__ __attribute__((aligned(1024))) u16 lds[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int block = w % NB;          // 32-row block
+    const int kg = w / NB;             // key group: even (0) or odd (1) tiles
+
+    const int N = args.N;
+    const float scale_log2 = args.scale_log2;
+    // Work item: longest causal query tiles first; consecutive workgroups
+    // are different heads of one query tile, dealt to the 8 XCDs so each XCD
+    // keeps a fixed set of heads in its L2.
+    const int bid = blockIdx.x;
+    const int tt = bid / args.BH;
+    const int t_q = CAUSAL ? (args.T - 1 - tt) : tt;
+    const int jh = bid % args.BH;
+    const int bh = (args.BH & 7) ? jh : (jh & 7) * (args.BH >> 3) + (jh >> 3);
+    const int kvh = (bh / args.H) * args.Hkv + (bh % args.H) / (args.H / args.Hkv);
+    const u16* __restrict__ q = args.q + (int64_t)bh * N * D;
+    const u16* __restrict__ k = args.k + (int64_t)kvh * N * D;
+    const u16* __restrict__ v = args.v + (int64_t)kvh * N * D;
+
+    const int row_base = t_q * BR;
+    int row0[QB];
+    row0[0] = row_base + 32 * block;
+    const int kv_end = CAUSAL ? min(row_base + BR, N) : N;
+    const int ntiles = (kv_end + G::BC - 1) / G::BC;
+    const int nsteps = (ntiles + 1) / 2;
+    // The wave's last tile with a visible key (none if its rows are past N).
+    const int last_live = row0[0] >= N ? -1
+                        : min(ntiles - 1, CAUSAL ? (row0[0] + 31) / G::BC : ntiles - 1);
+
+    WaveState<D, QB> st;
+    const int col = lane & 31, g = lane >> 5;
+    {
+        const int row = row0[0] + col;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            st.qf[0][ks] = row < N ? *reinterpret_cast<const u32x4*>(q + (int64_t)row * D + ks * 16 + 8 * g)
+                                   : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) st.acc[0][mt] = f32x16{};
+        st.m[0] = -INFINITY;
+        st.l[0] = 0.0f;
+    }
+    const FragOffsets<D> fo = frag_offsets<G>(lane);
+
+    auto stage = [&](int j) { return lds + (j & 1) * STAGE; };
+    // Copies of step j (tiles 2j and 2j+1), shared by all 8 waves.
+    auto issue = [&](int j) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int tile = 2 * j + s2;
+            if (tile < ntiles) {
+                u16* dst = stage(j) + s2 * SLOT;
+#pragma unroll
+                for (int c = 0; c < G::BPW; ++c) {
+                    if ((tile + 1) * G::BC <= N) {
+                        dma_block_full<G>(k, dst, tile, w, lane, c);
+                        dma_block_full<G>(v, dst + TILE, tile, w, lane, c);
+                    } else {
+                        dma_block<G>(k, dst, tile, N, w, lane, c);
+                        dma_block<G>(v, dst + TILE, tile, N, w, lane, c);
+                    }
+                }
+            }
+        }
+    };
+    // End of step j: the copies of step j+1 complete for this wave, then for all.
+    auto finish = [&]() {
+        wait_vmcnt<0>();
+        __syncthreads();
+    };
+
+    issue(0);
+    finish();
+    // Every wave runs all nsteps steps (copies and barriers), whatever it
+    // computes; the loops are split so each holds one code variant.  Stage
+    // (j+1) & 1, which step j's copies fill, held step j-1.
+    f32x16 s[QB][2];
+    int j = 0;
+    for (; 2 * j + kg < last_live; ++j) {
+        issue(j + 1);
+        const u16* kt = stage(j) + kg * SLOT;
+        qk_tile<BF16, G, QB>(st, fo, kt, s);
+        softmax_pv_tile<BF16, G, CAUSAL, false, QB>(st, fo, s, kt + TILE, lane, (2 * j + kg) * G::BC,
+                                                    row0, N, scale_log2);
+        finish();
+    }
+    if (j < nsteps && 2 * j + kg == last_live) {
+        issue(j + 1);
+        const u16* kt = stage(j) + kg * SLOT;
+        const int key0 = (2 * j + kg) * G::BC;
+        qk_tile<BF16, G, QB>(st, fo, kt, s);
+        if ((CAUSAL && key0 + G::BC - 1 > row0[0]) || key0 + G::BC > N)
+            softmax_pv_tile<BF16, G, CAUSAL, true, QB>(st, fo, s, kt + TILE, lane, key0, row0, N,
+                                                       scale_log2);
+        else
+            softmax_pv_tile<BF16, G, CAUSAL, false, QB>(st, fo, s, kt + TILE, lane, key0, row0, N,
+                                                        scale_log2);
+        finish();
+        ++j;
+    }
+    for (; j < nsteps; ++j) {
+        issue(j + 1);
+        finish();
+    }
+
+    // Merge: the odd-tile wave of each row block passes (o, m, l) to its
+    // partner through LDS (free after the last barrier), lane to lane, as
+    // 16-byte vectors (a lane's record is padded to 68 floats: a multiple of
+    // four, and lanes 4 banks apart).
+    constexpr int NR = MT * 16 + 4;
+    f32x4* xch = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(lds) + (block * 64 + lane) * NR);
+    if (kg == 1) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                xch[mt * 4 + i4] = f32x4{st.acc[0][mt][4 * i4], st.acc[0][mt][4 * i4 + 1],
+                                         st.acc[0][mt][4 * i4 + 2], st.acc[0][mt][4 * i4 + 3]};
+        xch[MT * 4] = f32x4{st.m[0], st.l[0], 0.0f, 0.0f};
+    }
+    __syncthreads();
+    if (kg == 1) return;
+    const f32x4 ml = xch[MT * 4];
+    const float m = fmaxf(st.m[0], ml[0]);
+    const float a0 = online_rescale(st.m[0], m);
+    const float a1 = online_rescale(ml[0], m);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 o1 = xch[mt * 4 + i4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                st.acc[0][mt][4 * i4 + e] = st.acc[0][mt][4 * i4 + e] * a0 + o1[e] * a1;
+        }
+    st.l[0] = st.l[0] * a0 + ml[1] * a1;
+    st.m[0] = m;
+    store_rows<D, QB>(st, args, 0, bh, row0, col, g);
+}
+
+// ---------------------------------------------------------------------------
 // Key-half unit kernel: 8 waves of 32 query rows (256 rows per workgroup, one
 // workgroup per CU), two waves per SIMD, all computing.
 //
@@ -1522,6 +1694,16 @@ hipError_t launch_pipe(AttnArgs a, hipStream_t stream) {
                            dim3((unsigned)(a.T * a.BH * a.nseg)), dim3(512), params, 0, stream);
 }
 
+template <bool BF16, int D, bool CAUSAL, int NW>
+hipError_t launch_ksplit(AttnArgs a, hipStream_t stream) {
+    constexpr int BR = 16 * NW;
+    a.T = (a.N + BR - 1) / BR;
+    a.scale_log2 = kLog2e / __builtin_sqrtf((float)D);
+    void* params[] = {(void*)&a};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_fwd_ksplit_kernel<BF16, D, CAUSAL, NW>),
+                           dim3((unsigned)(a.T * a.BH)), dim3(64 * NW), params, 0, stream);
+}
+
 template <bool BF16, int D, bool CAUSAL, int QB, int NWV>
 hipError_t launch_units(AttnArgs a, hipStream_t stream) {
     constexpr int RW = 32 * QB * NWV;
@@ -1545,10 +1727,15 @@ inline bool units_qb2(int64_t BH, int64_t N) { return BH * ((N + 511) / 512) >= 
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_cfg(const AttnArgs& a, int waves, hipStream_t stream) {
     if (waves == 4) {
-        if constexpr (D == 128)
+        if constexpr (D == 128) {
+            // At most two rounds of 64-row workgroups: the key split shortens
+            // the longest workgroup's walk over its keys (C2: 15 -> 11 us).
+            if (a.nseg == 1 && (int64_t)a.BH * ((a.N + 63) / 64) <= 512)
+                return launch_ksplit<BF16, D, CAUSAL, 4>(a, stream);
             return launch_ring<BF16, D, CAUSAL, 4, 2, 2, 1>(a, stream);
-        else
+        } else {
             return launch_ring<BF16, D, CAUSAL, 4, 2, 3, 2>(a, stream);
+        }
     }
     if constexpr (D == 64) {
         if (a.nseg == 1 && units_qb2(a.BH, a.N)) return launch_units<BF16, D, CAUSAL, 2, 8>(a, stream);
