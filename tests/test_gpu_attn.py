@@ -162,6 +162,43 @@ def test_identical_keys_give_prefix_mean_on_gpu():
 # D = 64); the small shapes above run 4-wave workgroups.  The pipeline kernel
 # runs its key tiles after the first in groups of four plus 0-3 more: the
 # shapes cover every remainder, ragged key tails and several query tiles.
+# Shapes on both sides of each kernel-selection boundary at D = 128: the
+# key-split kernel takes B*H*ceil(N/64) <= 512, the ring kernel up to
+# B*H*ceil(N/256) < 512, the pipeline kernel beyond.
+BOUNDARY = [
+    # (B, H, N, D, sigma_qk, kernel)
+    (1, 32, 1024, 128, 1.0, "key split, 512 workgroups"),
+    (1, 32, 1025, 128, 1.0, "ring, 33 64-row tiles per head"),
+    (2, 7, 2300, 128, 3.0, "key split, large logits, 504 workgroups"),
+    (1, 16, 2100, 128, 3.0, "ring, large logits, 528 64-row tiles"),
+    (1, 1, 32768, 128, 1.0, "key split, one head, 512 workgroups"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", BOUNDARY, ids=lambda s: "B%dH%dN%dD%d" % s[:4])
+def test_selection_boundaries_match_oracle(shape, causal, dtype):
+    B, H, N, D, sigma, _ = shape
+    seed = 2500 + N * 3 + B + (1 if causal else 0)
+    q, k, v = workloads.attn_inputs(B, H, N, D, dtype, seed, sigma_qk=sigma)
+    name = "boundary attn %s %s B%d H%d N%d D%d sigma %g seed %d" % (
+        "causal" if causal else "full", dtype, B, H, N, D, sigma, seed)
+    print("running", name, flush=True)
+    o, lse = run_gpu(q, k, v, causal, dtype)
+    if N > 4096:
+        # one head of 32768 rows: rows near the head's ends and tile edges, and
+        # a seeded spread through it (flat row ids; B = H = 1)
+        g = torch.Generator().manual_seed(seed)
+        rows = sorted({0, 1, 63, 64, N - 1} | set(torch.randint(0, N, (120,), generator=g).tolist()))
+        o_ref, lse_ref = oracle.attn_rows(q, k, v, causal, rows)
+        assert np.isfinite(o).all() and np.isfinite(lse).all()
+        check(name, o.reshape(-1, D)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, dtype)
+    else:
+        o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal)
+        check(name, o, lse, o_ref, lse_ref, dtype)
+
+
 WIDE = [
     # (B, H, N, D, sigma_qk)
     (1, 512, 64, 128, 1.0),     # one 64-key tile per head
