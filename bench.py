@@ -32,6 +32,15 @@ One JSON line goes to stdout.  Besides the contract fields it carries:
                 C3, C5, R1 and R2 also carry the FP64 oracle's parity on every
                 output element and its own timing beside the GPU's.
 Runs on one GPU only; --gpus above 1 exits with a message.
+
+    python bench.py --ceiling
+
+prints instead the sustained rate, GFX clock and socket power of the
+matrix-core ceiling probe (libosc_ceiling.so: MFMAs alone, with one LDS
+fragment read each, and with the softmax's per-score VALU work added) and of
+the C4 attention forward, each run back to back for a few seconds in the same
+process: under sustained MFMA load the firmware sets the clock by power and
+activity, so these are the rates the part sustains for each instruction mix.
 """
 import argparse
 import hashlib
@@ -520,6 +529,71 @@ def profile_bwd(launches=10):
           "algorithmic FLOP per launch", 2.5 * w.flops)
 
 
+def ceiling(seconds=3.0, pairs=2000):
+    """Sustained TFLOP/s, clock and power of the ceiling probe's three mixes
+    and of attn_fwd on C4, one after the other in this process."""
+    import ctypes
+    import torch
+    import online_softmax_causal_amd as osc
+    import workloads
+    path = os.path.join(ROOT, "online_softmax_causal_amd", "libosc_ceiling.so")
+    if not os.path.exists(path):
+        raise SystemExit("%s is missing: run python -m online_softmax_causal_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    lib.osc_ceiling_src_bytes.restype = ctypes.c_int64
+    lib.osc_ceiling_mfma_per_wg_iter.restype = ctypes.c_int
+    lib.osc_ceiling_launch.restype = ctypes.c_int
+    lib.osc_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(7)
+    n16 = lib.osc_ceiling_src_bytes() // 2
+    src = (torch.rand(n16, generator=gen) * 4.0 - 2.0).to(torch.float16).to(dev)
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(grid * 512, dtype=torch.float32, device=dev)
+    flops = float(grid) * lib.osc_ceiling_mfma_per_wg_iter() * pairs * 32768.0
+    stream = torch.cuda.current_stream().cuda_stream
+    mixes = ((0, "MFMA only (v_mfma_f32_32x32x16_f16, random fp16 operands)"),
+             (1, "MFMA + one 1 KiB LDS fragment read per MFMA per wave"),
+             (2, "MFMA + LDS read + fma, exp2, add, 1/2 fp16 pack per MFMA"))
+    rows = []
+    for mix, desc in mixes:
+        def step(mix=mix):
+            e = lib.osc_ceiling_launch(mix, src.data_ptr(), out.data_ptr(), grid, pairs, stream)
+            if e != 0:
+                raise RuntimeError("ceiling probe launch failed: %d" % e)
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        rows.append((desc, measure_clock(step, flops, seconds)))
+    w = workloads.ATTN["C4"]
+    q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
+    o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def attn():
+        osc.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.D, w.causal, w.dtype)
+    for _ in range(20):
+        attn()
+    torch.cuda.synchronize()
+    rows.append(("attn_fwd " + w.describe(), measure_clock(attn, w.flops, seconds)))
+    print("sustained matrix-core rate per instruction mix: %.1f s back-to-back runs, amdsmi sampling"
+          % seconds)
+    print("probe grid %d workgroups x 8 waves, %d iterations of 32 MFMAs per wave per launch" % (grid, pairs))
+    print("")
+    print("workload | TFLOP/s | % of 2516.6 | GFX MHz | W | % of peak at that clock")
+    for desc, c in rows:
+        if c is None:
+            print("%s | (amdsmi unavailable)" % desc)
+            continue
+        print("%s | %.1f | %.1f | %.0f | %.0f | %.1f" % (
+            desc, c["sustained_tflops"], 100.0 * c["sustained_tflops"] / PEAK_F16_TFLOPS, c["clock_mhz"],
+            c["power_w"] or float("nan"), 100.0 * c["frac_of_peak_at_clock"]))
+    print("")
+    print("sources_sha256_16: ceiling.hip %s, attn_fwd.hip+mfma_tile.hpp+online_merge.hpp %s"
+          % (kernel_source_hash(("ceiling.hip",)), kernel_source_hash()))
+
+
 def _pmc_rows(path):
     import csv
     import glob
@@ -745,6 +819,8 @@ def main():
                     help="only launch the 32K-context paged decode 30 times (for rocprofv3)")
     ap.add_argument("--profile-bwd", action="store_true",
                     help="only run the headline workload's backward 10 times (for rocprofv3)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="print the MFMA rate the power limit allows per instruction mix, and C4's")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
     ap.add_argument("--summarize-sq", nargs="+", metavar="DIR")
@@ -782,6 +858,9 @@ def main():
         return
     if args.profile_bwd:
         profile_bwd()
+        return
+    if args.ceiling:
+        ceiling()
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

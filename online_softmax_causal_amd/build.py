@@ -4,6 +4,9 @@
 
 Every HIP source is compiled to an object under ``_build/`` in parallel and
 the objects are linked into ``online_softmax_causal_amd/libosc_attn.so``.
+``csrc/ceiling.hip``, the matrix-core ceiling probe that ``bench.py
+--ceiling`` runs, is linked into its own ``libosc_ceiling.so``: it is
+measurement support, not part of the library's interface.
 Packed FP32 instructions are disabled for all device code.
 """
 from __future__ import annotations
@@ -19,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libosc_attn.so")
+CEILING_LIB = os.path.join(PKG, "libosc_ceiling.so")
 SOURCES = ["attn_fwd.hip", "bwd.hip", "decode.hip", "splitkv.hip", "row_softmax.hip", "api.hip",
            "noalloc.hip"]
 ARCH = "gfx950"
@@ -65,22 +69,31 @@ def check_m0(src: str) -> None:
                 raise RuntimeError("unexpected use of M0 in %s: %r" % (src, ln))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
-        m0 = [ex.submit(check_m0, src) for src in ("attn_fwd.hip", "decode.hip", "bwd.hip")]
-        objs = list(ex.map(_compile, SOURCES))
-        for f in m0:
-            f.result()
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link the shared library (and the ceiling
+    probe's); returns the library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 3) as ex:
+        m0 = [ex.submit(check_m0, src) for src in ("attn_fwd.hip", "decode.hip", "bwd.hip")]
+        ceiling = ex.submit(_compile, "ceiling.hip")
+        objs = list(ex.map(_compile, SOURCES))
+        for f in m0:
+            f.result()
+        ceiling_obj = ceiling.result()
+    _link(objs, LIB)
+    _link([ceiling_obj], CEILING_LIB)
     if verbose:
         print("built", LIB)
+        print("built", CEILING_LIB)
     return LIB
 
 

@@ -1,0 +1,129 @@
+// Matrix-core ceiling probe (measurement support for bench.py --ceiling; not
+// part of the attention library's interface).
+//
+// Under a sustained MFMA load this part does not hold its nominal 2.4 GHz:
+// the firmware lowers the GFX clock to stay within the board power limit and,
+// as the work per cycle grows, further (the probe's heavier mixes settle at
+// lower clocks while drawing less power).  The rate an MFMA-bound kernel can
+// reach therefore depends on the instructions it issues, not only on the
+// nominal peak.  This probe measures that rate for three fixed instruction
+// mixes, with the same MFMA (v_mfma_f32_32x32x16_f16), the same occupancy
+// (one 512-thread workgroup per CU, two waves per SIMD) and the same kind of
+// operand data (random fp16) as the attention forward kernel:
+//   mix 0  MFMAs only, four independent accumulator chains per wave;
+//   mix 1  mix 0 plus one 16-byte-per-lane LDS read per MFMA as its A operand
+//          (1 KiB per MFMA per wave: the forward kernel's K/V fragment bytes);
+//   mix 2  mix 1 plus, per MFMA, one FMA, one exp2 and one add on a value of
+//          another accumulator chain and, every second MFMA, one fp16 pack
+//          (the forward kernel's per-score softmax work: 32 scores per lane
+//          per 32 MFMAs).
+// bench.py runs each mix back to back while sampling clock and power.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 512;
+constexpr int kLdsVec = 6144;  // 96 KiB of 16-byte vectors: one workgroup per CU
+constexpr int kMfmaPerIter = 16;
+
+// One step: 16 MFMAs into accumulator set PH; with MIX >= 1 each takes its A
+// operand from a ring of 4 LDS fragments read 4 MFMAs ahead; with MIX = 2 the
+// VALU work reads set PH ^ 1, written by the previous step (so it never waits
+// on an MFMA in flight, as the softmax of a finished tile does not).
+template <int MIX, int PH>
+__device__ __forceinline__ void ceiling_step(f32x16 (&c)[2][4], f16x8 (&ring)[4], const f16x8& a,
+                                             const f16x8& b, const f16x8 __attribute__((address_space(3)))* base,
+                                             float& sum, float& p0) {
+#pragma unroll
+    for (int m = 0; m < kMfmaPerIter; ++m) {
+        const f16x8 av = MIX >= 1 ? ring[m & 3] : a;
+        c[PH][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b, c[PH][m & 3], 0, 0, 0);
+        if constexpr (MIX >= 1) ring[m & 3] = base[256 * ((m + 4) & 15)];
+        if constexpr (MIX >= 2) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(c[PH ^ 1][m >> 2][m], 1.0e-4f, -0.5f));
+            sum += p;
+            if (m & 1) {
+                f16x2 pk;
+                pk[0] = (_Float16)p0;
+                pk[1] = (_Float16)p;
+                asm volatile("" ::"v"(pk));
+            } else {
+                p0 = p;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int MIX>
+__global__ void __launch_bounds__(kThreads, 1)
+ceiling_kernel(const f16x8* __restrict__ src, float* __restrict__ out, int pairs) {
+    typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
+    __shared__ f16x8 lds[kLdsVec];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kLdsVec; i += kThreads) lds[i] = src[i];
+    __syncthreads();
+    const f16x8 a = src[tid];
+    const f16x8 b = src[kThreads + tid];
+    f32x16 c[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) c[h][j][e] = (float)src[2 * kThreads + tid][(e + j + h) & 7];
+    float sum = 0.0f, p0 = 0.0f;
+    // Lane reads base[256 m], m < 16: vectors below 511 + 3840 < kLdsVec.
+    const lds_f16x8* base = (const lds_f16x8*)lds + tid;
+    f16x8 ring[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ring[r] = MIX >= 1 ? base[256 * r] : a;
+    for (int it = 0; it < pairs; ++it) {
+        // Opaque per iteration, so the LDS reads are not hoisted out of the loop.
+        asm volatile("" : "+v"(base));
+        ceiling_step<MIX, 0>(c, ring, a, b, base, sum, p0);
+        ceiling_step<MIX, 1>(c, ring, a, b, base, sum, p0);
+    }
+    float r = sum;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r += c[h][j][e];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r += (float)ring[q][q];
+    out[(int64_t)blockIdx.x * kThreads + tid] = r;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Bytes of fp16 source data the probe reads (random values, caller-filled).
+int64_t osc_ceiling_src_bytes() { return (int64_t)kLdsVec * 16; }
+
+// MFMAs one launch issues per workgroup and iteration (x 32768 FLOP each).
+int osc_ceiling_mfma_per_wg_iter() { return (kThreads / 64) * 2 * kMfmaPerIter; }
+
+// Enqueue one launch of mix `mix` (0, 1, 2) on `stream`: `grid` workgroups of
+// `iters` iterations (of 2 x 16 MFMAs per wave) each.  src: device buffer of osc_ceiling_src_bytes()
+// bytes; out: device buffer of grid * 512 floats.  Returns a hipError_t
+// value (hipErrorInvalidValue for a bad argument, nothing enqueued).
+int osc_ceiling_launch(int mix, const void* src, float* out, int grid, int iters, hipStream_t stream) {
+    if (!src || !out || grid < 1 || iters < 1 || mix < 0 || mix > 2) return (int)hipErrorInvalidValue;
+    const f16x8* s = static_cast<const f16x8*>(src);
+    void* params[] = {(void*)&s, (void*)&out, (void*)&iters};
+    const void* fn = mix == 0 ? reinterpret_cast<const void*>(&ceiling_kernel<0>)
+                   : mix == 1 ? reinterpret_cast<const void*>(&ceiling_kernel<1>)
+                              : reinterpret_cast<const void*>(&ceiling_kernel<2>);
+    return (int)hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
+}
+
+}  // extern "C"

@@ -41,6 +41,25 @@ def test_every_bound_entry_point_is_declared():
     assert set(osc.EXPORTS) == declared_functions()
 
 
+def test_ceiling_probe_library_loads_and_rejects_bad_arguments():
+    """The matrix-core ceiling probe that bench.py --ceiling runs is a library
+    of its own (not part of the declared interface): it loads, reports its
+    sizes, and refuses bad arguments before anything is launched."""
+    path = os.path.join(ROOT, "online_softmax_causal_amd", "libosc_ceiling.so")
+    assert os.path.exists(path), "run python -m online_softmax_causal_amd.build"
+    lib = ctypes.CDLL(path)
+    lib.osc_ceiling_src_bytes.restype = ctypes.c_int64
+    lib.osc_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p]
+    assert lib.osc_ceiling_src_bytes() == 6144 * 16
+    assert lib.osc_ceiling_mfma_per_wg_iter() == 8 * 32
+    invalid = 1  # hipErrorInvalidValue
+    for mix, src, out, grid, iters in ((3, BASE, BASE, 1, 1), (-1, BASE, BASE, 1, 1),
+                                       (0, None, BASE, 1, 1), (0, BASE, None, 1, 1),
+                                       (0, BASE, BASE, 0, 1), (0, BASE, BASE, 1, 0)):
+        assert lib.osc_ceiling_launch(mix, src, out, grid, iters, None) == invalid
+
+
 def test_status_strings():
     for code in osc.STATUS:
         s = osc.attn_status_str(code)
