@@ -1216,8 +1216,9 @@ __global__ void __launch_bounds__(64 * NWV, 1) attn_fwd_units_kernel(AttnArgs ar
 // half 0 at the start of iteration i and key half 1 once its QK is done, only
 // for tiles that need it: the four diagonal tiles
 // of the workgroup and a ragged last tile.  A tile wholly above a wave's rows
-// is fully masked (P = 0) and still computed, while the other waves of the
-// workgroup work on it.
+// is fully masked (P = 0); the wave still computes it while it has other work
+// in the same iteration, and skips every iteration from the one where none is
+// left (it then only copies and meets the barriers).
 template <bool BF16, int D, bool CAUSAL>
 __global__ void __launch_bounds__(512, 1) attn_fwd_pipe_kernel(AttnArgs args) {
     constexpr int QB = 1;             // 32-row blocks per wave
@@ -1246,8 +1247,10 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_pipe_kernel(AttnArgs args) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Waves w and w + 4 share a SIMD and take adjacent 32-row blocks.
-    const int block0 = 2 * (w & 3) + (w >> 2);
+    // Waves w and w + 4 share a SIMD (w mod 4) and take 32-row blocks w mod 4
+    // and 7 - w mod 4: on the causal diagonal the waves of the early blocks
+    // run out of work first, and each SIMD then keeps one busy wave.
+    const int block0 = w < 4 ? w : 11 - w;
 
     const int N = args.N;
     const float scale_log2 = args.scale_log2;
@@ -1646,7 +1649,14 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_pipe_kernel(AttnArgs args) {
     iteration(P0{}, Y{}, F{}, Y{}, kt0);
     // Iterations kt0+1 .. T: QK of key half 0 of tile T+1 (in the last one)
     // reads a stage holding no valid tile and its result is never used.
-    const int nmid = T - kt0;
+    // With causal masking a wave has no work left from iteration i_idle on:
+    // every key of tile i_idle - 1 and later lies after its last row
+    // (64 (i_idle - 1) >= row0 + 32), so those tiles' scores are all masked,
+    // their P is zero and the PV products add nothing.  From there the wave
+    // only issues its share of the copies and meets the barriers.
+    const int i_idle = CAUSAL ? (row0[0] + 96 + G::BC - 1) / G::BC : T + 2;
+    const int Tw = min(T, i_idle - 1);  // this wave's last iteration with work
+    const int nmid = max(Tw - kt0, 0);
     const int nq = nmid / 4;
     int i = kt0 + 1;
     for (int qq = 0; qq < nq; ++qq, i += 4) {
@@ -1659,12 +1669,28 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_pipe_kernel(AttnArgs args) {
     if (nr >= 1) iteration(P1{}, Y{}, Y{}, Y{}, i++);
     if (nr >= 2) iteration(P2{}, Y{}, Y{}, Y{}, i++);
     if (nr >= 3) iteration(P3{}, Y{}, Y{}, Y{}, i++);
-    // PV(T): the PV half of the iteration after T.
-    switch (nr) {
-        case 0: iteration(P1{}, F{}, Y{}, F{}, i); break;
-        case 1: iteration(P2{}, F{}, Y{}, F{}, i); break;
-        case 2: iteration(P3{}, F{}, Y{}, F{}, i); break;
-        default: iteration(P0{}, F{}, Y{}, F{}, i); break;
+    // Idle iterations: the copies of iteration i (K(i+3), V(i+2)), then the
+    // iteration's wait and barrier.
+    for (; i <= T; ++i) {
+        const int ph = (i - kt0) & 3;
+#pragma unroll
+        for (int c = 0; c < 2 * BPW; ++c) copy_part(ph, i, c);
+        if (i + 3 <= T)
+            wait_vmcnt<2 * BPW>();
+        else if (i + 2 <= T)
+            wait_vmcnt<BPW>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+    }
+    // PV(T): the PV half of the iteration after T (nothing for a wave idle there).
+    if (i_idle > T + 1) {
+        switch (nr) {
+            case 0: iteration(P1{}, F{}, Y{}, F{}, i); break;
+            case 1: iteration(P2{}, F{}, Y{}, F{}, i); break;
+            case 2: iteration(P3{}, F{}, Y{}, F{}, i); break;
+            default: iteration(P0{}, F{}, Y{}, F{}, i); break;
+        }
     }
 
     store_rows<D, QB>(st, args, seg, bh, row0, col, g);
