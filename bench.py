@@ -555,7 +555,8 @@ def ceiling(seconds=3.0, pairs=2000):
     stream = torch.cuda.current_stream().cuda_stream
     mixes = ((0, "MFMA only (v_mfma_f32_32x32x16_f16, random fp16 operands)"),
              (1, "MFMA + one 1 KiB LDS fragment read per MFMA per wave"),
-             (2, "MFMA + LDS read + fma, exp2, add, 1/2 fp16 pack per MFMA"))
+             (2, "MFMA + LDS read + fma, exp2, add, 1/2 fp16 pack per MFMA"),
+             (3, "MFMA + LDS read + 2 x (fma, exp2, add), 1 fp16 pack per MFMA"))
     rows = []
     for mix, desc in mixes:
         def step(mix=mix):
@@ -566,17 +567,36 @@ def ceiling(seconds=3.0, pairs=2000):
             step()
         torch.cuda.synchronize()
         rows.append((desc, measure_clock(step, flops, seconds)))
+    for name in ("C4", "C5"):
+        w = workloads.ATTN[name]
+        q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
+        o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def attn(w=w, q=q, k=k, v=v, o=o, lse=lse):
+            osc.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.D, w.causal, w.dtype)
+        for _ in range(20):
+            attn()
+        torch.cuda.synchronize()
+        rows.append(("attn_fwd " + w.describe(), measure_clock(attn, w.flops, seconds)))
+        del q, k, v, o, lse
+    # C4 backward: algorithmic FLOP (five products, 2.5x the forward's).
     w = workloads.ATTN["C4"]
-    q, k, v = (t.to(dev) for t in workloads.workload_inputs(w))
+    q, k, v, do = (t.to(dev) for t in workloads.bwd_inputs(w.B, w.H, w.N, w.D, w.dtype, w.seed))
     o = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    osc.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.D, w.causal, w.dtype)
+    grads = [torch.empty_like(o) for _ in range(3)]
+    need = osc.attn_bwd_workspace(w.B, w.H, w.N)
+    ws = torch.empty((need // 4,), dtype=torch.float32, device=dev)
 
-    def attn():
-        osc.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.D, w.causal, w.dtype)
-    for _ in range(20):
-        attn()
+    def bwd():
+        osc.attn_bwd(q, k, v, o, lse, do, *grads, w.B, w.H, w.N, w.D, w.causal, w.dtype, ws, need)
+    for _ in range(3):
+        bwd()
     torch.cuda.synchronize()
-    rows.append(("attn_fwd " + w.describe(), measure_clock(attn, w.flops, seconds)))
+    rows.append(("attn_bwd " + w.describe().replace("fwd", "bwd") + " (algorithmic FLOP)",
+                 measure_clock(bwd, 2.5 * w.flops, seconds)))
     print("sustained matrix-core rate per instruction mix: %.1f s back-to-back runs, amdsmi sampling"
           % seconds)
     print("probe grid %d workgroups x 8 waves, %d iterations of 32 MFMAs per wave per launch" % (grid, pairs))

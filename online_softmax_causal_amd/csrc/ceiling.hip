@@ -6,7 +6,7 @@
 // as the work per cycle grows, further (the probe's heavier mixes settle at
 // lower clocks while drawing less power).  The rate an MFMA-bound kernel can
 // reach therefore depends on the instructions it issues, not only on the
-// nominal peak.  This probe measures that rate for three fixed instruction
+// nominal peak.  This probe measures that rate for four fixed instruction
 // mixes, with the same MFMA (v_mfma_f32_32x32x16_f16), the same occupancy
 // (one 512-thread workgroup per CU, two waves per SIMD) and the same kind of
 // operand data (random fp16) as the attention forward kernel:
@@ -15,8 +15,10 @@
 //          (1 KiB per MFMA per wave: the forward kernel's K/V fragment bytes);
 //   mix 2  mix 1 plus, per MFMA, one FMA, one exp2 and one add on a value of
 //          another accumulator chain and, every second MFMA, one fp16 pack
-//          (the forward kernel's per-score softmax work: 32 scores per lane
-//          per 32 MFMAs).
+//          (the forward kernel's per-score softmax work at D = 128: 32 scores
+//          per lane per 32 MFMAs);
+//   mix 3  mix 1 plus that work on two values per MFMA and one pack per MFMA
+//          (the score density at D = 64: 64 scores per lane per 32 MFMAs).
 // bench.py runs each mix back to back while sampling clock and power.
 #include <hip/hip_runtime.h>
 
@@ -45,10 +47,14 @@ __device__ __forceinline__ void ceiling_step(f32x16 (&c)[2][4], f16x8 (&ring)[4]
         const f16x8 av = MIX >= 1 ? ring[m & 3] : a;
         c[PH][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b, c[PH][m & 3], 0, 0, 0);
         if constexpr (MIX >= 1) ring[m & 3] = base[256 * ((m + 4) & 15)];
-        if constexpr (MIX >= 2) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(c[PH ^ 1][m >> 2][m], 1.0e-4f, -0.5f));
+        // Values per MFMA: 1 (mix 2) or 2 (mix 3); a pack per two values.
+        constexpr int VPM = MIX == 2 ? 1 : MIX == 3 ? 2 : 0;
+#pragma unroll
+        for (int v = 0; v < VPM; ++v) {
+            const int x = m * VPM + v;  // < 32: chains 0 and 1 of the other set
+            const float p = __builtin_amdgcn_exp2f(fmaf(c[PH ^ 1][x >> 4][x & 15], 1.0e-4f, -0.5f));
             sum += p;
-            if (m & 1) {
+            if (x & 1) {
                 f16x2 pk;
                 pk[0] = (_Float16)p0;
                 pk[1] = (_Float16)p;
@@ -112,17 +118,18 @@ int64_t osc_ceiling_src_bytes() { return (int64_t)kLdsVec * 16; }
 // MFMAs one launch issues per workgroup and iteration (x 32768 FLOP each).
 int osc_ceiling_mfma_per_wg_iter() { return (kThreads / 64) * 2 * kMfmaPerIter; }
 
-// Enqueue one launch of mix `mix` (0, 1, 2) on `stream`: `grid` workgroups of
+// Enqueue one launch of mix `mix` (0 to 3) on `stream`: `grid` workgroups of
 // `iters` iterations (of 2 x 16 MFMAs per wave) each.  src: device buffer of osc_ceiling_src_bytes()
 // bytes; out: device buffer of grid * 512 floats.  Returns a hipError_t
 // value (hipErrorInvalidValue for a bad argument, nothing enqueued).
 int osc_ceiling_launch(int mix, const void* src, float* out, int grid, int iters, hipStream_t stream) {
-    if (!src || !out || grid < 1 || iters < 1 || mix < 0 || mix > 2) return (int)hipErrorInvalidValue;
+    if (!src || !out || grid < 1 || iters < 1 || mix < 0 || mix > 3) return (int)hipErrorInvalidValue;
     const f16x8* s = static_cast<const f16x8*>(src);
     void* params[] = {(void*)&s, (void*)&out, (void*)&iters};
-    const void* fn = mix == 0 ? reinterpret_cast<const void*>(&ceiling_kernel<0>)
+    const void* fn = mix == 0   ? reinterpret_cast<const void*>(&ceiling_kernel<0>)
                    : mix == 1 ? reinterpret_cast<const void*>(&ceiling_kernel<1>)
-                              : reinterpret_cast<const void*>(&ceiling_kernel<2>);
+                   : mix == 2 ? reinterpret_cast<const void*>(&ceiling_kernel<2>)
+                              : reinterpret_cast<const void*>(&ceiling_kernel<3>);
     return (int)hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
 }
 

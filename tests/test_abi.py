@@ -54,7 +54,7 @@ def test_ceiling_probe_library_loads_and_rejects_bad_arguments():
     assert lib.osc_ceiling_src_bytes() == 6144 * 16
     assert lib.osc_ceiling_mfma_per_wg_iter() == 8 * 32
     invalid = 1  # hipErrorInvalidValue
-    for mix, src, out, grid, iters in ((3, BASE, BASE, 1, 1), (-1, BASE, BASE, 1, 1),
+    for mix, src, out, grid, iters in ((4, BASE, BASE, 1, 1), (-1, BASE, BASE, 1, 1),
                                        (0, None, BASE, 1, 1), (0, BASE, None, 1, 1),
                                        (0, BASE, BASE, 0, 1), (0, BASE, BASE, 1, 0)):
         assert lib.osc_ceiling_launch(mix, src, out, grid, iters, None) == invalid
