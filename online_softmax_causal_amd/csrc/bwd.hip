@@ -17,12 +17,15 @@
 // Three kernels, all on one stream:
 //   attn_bwd_pre_kernel   D_i and the base-2 log-sum-exp lse_i * log2(e) of
 //                         every row, into the caller's workspace (HBM-bound);
-//   attn_bwd_dkdv_kernel  key-major: a workgroup keeps 32 keys per wave (4
-//                         waves at D = 128, 8 at D = 64) of one K/V head in
-//                         registers and streams 64-row tiles of Q and dO
-//                         (with D and lse of those rows) of every query head
-//                         of the group through LDS;
-//                         dV^T += dO^T P and dK^T += Q^T dS on the MFMA;
+//   dK/dV kernel          key-major: a workgroup keeps 32 keys per wave of
+//                         one K/V head in registers and streams 64-row tiles
+//                         of Q and dO (with D and lse of those rows) of every
+//                         query head of the group through LDS;
+//                         dV^T += dO^T P and dK^T += Q^T dS on the MFMA.
+//                         D = 64: attn_bwd_dkdv_kernel, 8 waves (two per
+//                         SIMD), one 32-query block after the other;
+//                         D = 128: attn_bwd_dkdv_pipe_kernel, 4 waves (one
+//                         per SIMD), the blocks software-pipelined;
 //   attn_bwd_dq_kernel    query-major, like the forward kernel: a workgroup of
 //                         8 waves (two per SIMD) keeps 256 query rows of Q and
 //                         dO in registers and streams 64-key tiles of K and V,
@@ -546,6 +549,307 @@ attn_bwd_dq_kernel(BwdArgs a) {
                       dq_acc[mt][4 * i4 + 3]} * a.scale;
 }
 
+// ---------------------------------------------------------------------------
+// dK/dV at D = 128 as a software pipeline over 32-query blocks.  Same work,
+// layout and per-block arithmetic as attn_bwd_dkdv_kernel (one wave per SIMD,
+// 32 keys per wave with K^T and V^T resident), but the step of block j runs
+//   (a) if block j needs the mask: S_j set to -inf where key > query or the
+//       query row is past N (a wave-uniform branch once S_j is done);
+//   (b) S and dP of block j on the MFMA (16 MFMAs, the two products
+//       alternating, A operands through a 4-deep LDS ring);
+//   (c) dV^T += dO^T P and dK^T += Q^T dS of block j-1 (16 MFMAs,
+//       transposed LDS reads through a 4-deep ring), with block j's weights
+//       hosted between them: P = 2^(S scale - lse2), dS = P (dP - D), both
+//       packed to 16 bits.
+// Blocks 0 and 1 of a streamed tile are its two 32-row halves; block 0's
+// step finishes block 1 of the previous tile, so four LDS stages hold the
+// tile being read, the previous one (its last dV/dK) and two in flight.
+// Even and odd blocks keep packed P and dS in separate registers (the loop
+// body holds both steps of a tile), so no value moves between iterations.
+template <bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+attn_bwd_dkdv_pipe_kernel(BwdArgs a) {
+    constexpr int D = 128, NW = 4;
+    using M = Mma<BF16>;
+    constexpr int KS = D / 16, MT = D / 32;
+    constexpr int TILE = kBwdTile * D;
+    constexpr int STAGE = 2 * TILE + 2 * kBwdTile * 2;  // Q, dO (16-bit), lse2, D (FP32)
+    constexpr int LPM = copies_per_matrix<D, NW>();
+    constexpr int NSTG = 4;  // stages: tile t read, t-1 still read by dV/dK, t+1 and t+2 in flight
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    typedef __attribute__((address_space(3))) u16 lds_u16;
+    __shared__ __attribute__((aligned(1024))) u16 lds[NSTG * STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 31, g = lane >> 5;
+    const int N = a.N;
+    constexpr int kRows = 32 * NW;
+    const int nkt = (N + kRows - 1) / kRows;
+    int kt, bkv;
+    bwd_work(blockIdx.x, a.BHkv, nkt, false, &kt, &bkv);
+    const int64_t head = (int64_t)bkv * N;   // K/V / dK / dV rows of this head
+    const int grp = a.H / a.Hkv;
+    const int hq0 = (bkv / a.Hkv) * a.H + (bkv % a.Hkv) * grp;  // first query head
+    const int kw = kt * kRows + 32 * w;  // first key of this wave
+    const int key = kw + col;
+
+    // K^T and V^T fragments (B operands): lane (col, g) holds key `key`,
+    // d = 16 ks + 8 g .. + 7.
+    u32x4 kf[KS], vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int64_t off = (head + key) * D + ks * 16 + 8 * g;
+        kf[ks] = key < N ? *reinterpret_cast<const u32x4*>(a.k + off) : u32x4{0u, 0u, 0u, 0u};
+        vf[ks] = key < N ? *reinterpret_cast<const u32x4*>(a.v + off) : u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x16 dk_acc[MT], dv_acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        dk_acc[mt] = f32x16{};
+        dv_acc[mt] = f32x16{};
+    }
+    int rfo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) rfo[ks] = row_frag_offset<D>(col, ks, lane);
+    int tfo[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) tfo[mt][r] = tr_frag_offset<D>(lane, mt, r);
+
+    // Query tiles: with causal masking only rows at or after the workgroup's
+    // first key contribute.  Streamed tiles fi = i * nt + (it - qt0) for
+    // query head hq0 + i of the group and query tile it.
+    const int nqt = (N + kBwdTile - 1) / kBwdTile;
+    const int qt0 = CAUSAL ? (kt * kRows) / kBwdTile : 0;
+    const int nt = nqt - qt0;
+    const int nflat = grp * nt;
+    auto stage_off = [&](int fi) { return (fi % NSTG) * STAGE; };
+    auto tile_row0 = [&](int fi) { return (qt0 + fi % nt) * kBwdTile; };
+    // Waves 0 and 1 also copy the tile's lse2 and D rows (one 4-byte copy each).
+    auto issue = [&](int fi) {
+        if (fi >= nflat) return;
+        u16* st = lds + stage_off(fi);
+        const int64_t qhead = (int64_t)(hq0 + fi / nt) * N;
+        const int r0 = tile_row0(fi);
+        copy_tile<D, NW>(a.q + qhead * D, st, r0, N, w, lane);
+        copy_tile<D, NW>(a.dout + qhead * D, st + TILE, r0, N, w, lane);
+        if (w < 2) {
+            const int row = min(r0 + lane, N - 1);
+            const float* src = w == 0 ? a.lse2 + qhead : a.dd + qhead;
+            copy_to_lds4(src, (unsigned)(row * 4), st + 2 * TILE + w * 2 * kBwdTile);
+        }
+    };
+
+    // Per-lane LDS pointers, rebased once per tile: row fragments (read by
+    // S and dP; advanced to the next tile at its barrier) and transposed
+    // fragments plus this lane's lse2 / D entries (read by the weights and by
+    // dV, dK; advanced after a tile's last step).  Every fragment is a
+    // pointer plus an immediate.
+    const lds_u32x4* rp[KS];
+    const lds_s16x4* tp[MT][2];
+    const lds_f32x4* lp;
+    auto rebase_rows = [&](int fi) {
+        const int so = stage_off(fi);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            rp[ks] = (const lds_u32x4*)((const lds_u16*)lds + so + rfo[ks]);
+            asm volatile("" : "+v"(rp[ks]));
+        }
+        lp = (const lds_f32x4*)((const lds_u16*)lds + so + 2 * TILE) + g;
+        asm volatile("" : "+v"(lp));
+    };
+    auto rebase_trans = [&](int fi) {
+        const int so = stage_off(fi);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                tp[mt][r] = (const lds_s16x4*)((const lds_u16*)lds + so + tfo[mt][r]);
+                asm volatile("" : "+v"(tp[mt][r]));
+            }
+    };
+    // Row fragment ks of block b of the Q (X = 0) or dO (X = 1) tile.
+    auto rfrag = [&](int X, int b, int ks) __attribute__((always_inline)) {
+        return rp[ks][(X * TILE + b * 32 * D) / 8];
+    };
+    // Transposed fragment (16-row group u, d block mt) of block b of the Q
+    // (X = 0) or dO (X = 1) tile.
+    auto tfrag = [&](int X, int b, int u, int mt) __attribute__((always_inline)) {
+        const int o = (X * TILE + b * 32 * D + u * 16 * D) / 4;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp[mt][0] + o));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp[mt][1] + o));
+        const auto lo = __builtin_bit_cast(unsigned long long, x0);
+        const auto hi = __builtin_bit_cast(unsigned long long, x1);
+        return u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi, (unsigned)(hi >> 32)};
+    };
+
+    // Mask of block rows qb .. qb+31 (lane rows qb + 4g + off, off = 8(e/4) + e%4).
+    auto needs_mask = [&](int qb) __attribute__((always_inline)) {
+        return (CAUSAL && qb < kw + 31) || qb + 32 > N;
+    };
+    auto mask_s = [&](f32x16& s, int qb) __attribute__((always_inline)) {
+        const int lo = CAUSAL ? key - qb - 4 * g : -1;
+        const int hi = N - qb - 4 * g;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int off = 8 * (e >> 2) + (e & 3);
+            s[e] = (off < lo || off >= hi) ? -INFINITY : s[e];
+        }
+    };
+
+    f32x16 sc, dpc;            // S and dP of the current block
+    u32x4 pf0[2], dsf0[2], pf1[2], dsf1[2];  // packed P, dS of even / odd blocks
+    u32x4 ring[4];
+
+    // S and dP of block b of the tile behind rp: fragment f is the S product
+    // (ks = f/2) for even f, the dP product for odd f.
+    auto products = [&](int b) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) ring[f] = rfrag(f & 1, b, f >> 1);
+#pragma unroll
+        for (int f = 0; f < 2 * KS; ++f) {
+            const u32x4 x = ring[f & 3];
+            if (f + 4 < 2 * KS) ring[f & 3] = rfrag((f + 4) & 1, b, (f + 4) >> 1);
+            if (f & 1)
+                dpc = M::run(x, vf[f >> 1], f < 2 ? f32x16{} : dpc);
+            else
+                sc = M::run(x, kf[f >> 1], f < 2 ? f32x16{} : sc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Weights of the current block b (rows qb.., lse2 / D behind lp) into
+    // (pf, dsf); with PREV, hosted between the 16 MFMAs of dV^T += dO^T P and
+    // dK^T += Q^T dS of the previous block pb (tile behind tp) from (pfp,
+    // dsfp): fragment f is dV (even) or dK (odd) of pair (u, mt) =
+    // ((f/2) / MT, (f/2) % MT); element e of the weights runs after MFMA e.
+    auto weights = [&](auto prev_c, int b, int qb, u32x4 (&pf)[2], u32x4 (&dsf)[2], int pb,
+                       const u32x4 (&pfp)[2], const u32x4 (&dsfp)[2]) __attribute__((always_inline)) {
+        constexpr bool PREV = decltype(prev_c)::value;
+        if (needs_mask(qb)) mask_s(sc, qb);
+        float p[16], ds[16];
+        f32x4 l2, dd;
+        auto host = [&](int e) __attribute__((always_inline)) {
+            const int j4 = e >> 2, i = e & 3;
+            if (i == 0) {
+                l2 = lp[(32 * b + 8 * j4) / 4];
+                dd = lp[(kBwdTile + 32 * b + 8 * j4) / 4];
+            }
+            p[e] = fast_exp2(fmaf(sc[e], a.scale_log2, -l2[i]));
+            ds[e] = p[e] * (dpc[e] - dd[i]);
+            // Anchor each result where it is computed, so the work stays
+            // spread over the MFMA stream instead of sinking to its use.
+            asm volatile("" ::"v"(p[e]), "v"(ds[e]));
+            if (e & 1) {
+                const int u = e >> 3, q = (e & 7) >> 1;
+                pf[u][q] = M::pack(p[e - 1], p[e]);
+                dsf[u][q] = M::pack(ds[e - 1], ds[e]);
+                asm volatile("" ::"v"(pf[u][q]), "v"(dsf[u][q]));
+            }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PREV) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) ring[f] = tfrag(1 - (f & 1), pb, (f >> 1) / MT, (f >> 1) % MT);
+#pragma unroll
+            for (int f = 0; f < 4 * MT; ++f) {
+                const u32x4 x = ring[f & 3];
+                const int nf = f + 4;
+                if (nf < 4 * MT) ring[f & 3] = tfrag(1 - (nf & 1), pb, (nf >> 1) / MT, (nf >> 1) % MT);
+                const int u = (f >> 1) / MT, mt = (f >> 1) % MT;
+                if (f & 1)
+                    dk_acc[mt] = M::run(x, dsfp[u], dk_acc[mt]);
+                else
+                    dv_acc[mt] = M::run(x, pfp[u], dv_acc[mt]);
+                host(f);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) host(e);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // dV, dK of block pb alone (the last block).
+    auto finish = [&](int pb, const u32x4 (&pfp)[2], const u32x4 (&dsfp)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) ring[f] = tfrag(1 - (f & 1), pb, (f >> 1) / MT, (f >> 1) % MT);
+#pragma unroll
+        for (int f = 0; f < 4 * MT; ++f) {
+            const u32x4 x = ring[f & 3];
+            const int nf = f + 4;
+            if (nf < 4 * MT) ring[f & 3] = tfrag(1 - (nf & 1), pb, (nf >> 1) / MT, (nf >> 1) % MT);
+            const int u = (f >> 1) / MT, mt = (f >> 1) % MT;
+            if (f & 1)
+                dk_acc[mt] = M::run(x, dsfp[u], dk_acc[mt]);
+            else
+                dv_acc[mt] = M::run(x, pfp[u], dv_acc[mt]);
+        }
+    };
+    std::integral_constant<bool, true> prev;
+    std::integral_constant<bool, false> none;
+
+    // Tile fi complete for all waves, tile fi+1's copies (if any) still in
+    // flight; then the copies of tile fi+2 into the stage of tile fi-2,
+    // whose last reads (dV/dK of its block 1) ran in the first step of tile
+    // fi-1.
+    auto arrive = [&](int fi) {
+        if (fi + 1 < nflat) {
+            if (w < 2)
+                wait_vmcnt<2 * LPM + 1>();
+            else
+                wait_vmcnt<2 * LPM>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+        issue(fi + 2);
+    };
+    issue(0);
+    issue(1);
+    arrive(0);
+    rebase_rows(0);
+    rebase_trans(0);
+    // Tile 0: block 0 has no predecessor.
+    int qb = tile_row0(0);
+    products(0);
+    weights(none, 0, qb, pf0, dsf0, 0, pf1, dsf1);
+    products(1);
+    weights(prev, 1, qb + 32, pf1, dsf1, 0, pf0, dsf0);
+    for (int fi = 1; fi < nflat; ++fi) {
+        arrive(fi);
+        rebase_rows(fi);
+        qb = tile_row0(fi);
+        products(0);
+        weights(prev, 0, qb, pf0, dsf0, 1, pf1, dsf1);   // dV/dK of block 1 of tile fi-1
+        rebase_trans(fi);
+        products(1);
+        weights(prev, 1, qb + 32, pf1, dsf1, 0, pf0, dsf0);
+    }
+    finish(1, pf1, dsf1);
+
+    // Lane (col, g) holds d = 32 mt + 8 (i / 4) + 4 g + i % 4 of key `key`.
+    if (key >= N) return;
+    float* dkr = a.dk + (head + key) * D;
+    float* dvr = a.dv + (head + key) * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int d = mt * 32 + 8 * i4 + 4 * g;
+            *reinterpret_cast<f32x4*>(dkr + d) =
+                f32x4{dk_acc[mt][4 * i4], dk_acc[mt][4 * i4 + 1], dk_acc[mt][4 * i4 + 2],
+                      dk_acc[mt][4 * i4 + 3]} * a.scale;
+            *reinterpret_cast<f32x4*>(dvr + d) =
+                f32x4{dv_acc[mt][4 * i4], dv_acc[mt][4 * i4 + 1], dv_acc[mt][4 * i4 + 2],
+                      dv_acc[mt][4 * i4 + 3]};
+        }
+}
+
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_bwd(BwdArgs a, hipStream_t stream) {
     void* params[] = {(void*)&a};
@@ -556,8 +860,9 @@ hipError_t launch_bwd(BwdArgs a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     constexpr int kv_rows = 32 * dkdv_waves<D>();
     const unsigned grid = (unsigned)(((a.N + kv_rows - 1) / kv_rows) * a.BHkv);
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<BF16, D, CAUSAL>),
-                        dim3(grid), dim3(64 * dkdv_waves<D>()), params, 0, stream);
+    const void* dkdv = D == 128 ? reinterpret_cast<const void*>(&attn_bwd_dkdv_pipe_kernel<BF16, CAUSAL>)
+                                : reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<BF16, D, CAUSAL>);
+    e = hipLaunchKernel(dkdv, dim3(grid), dim3(64 * dkdv_waves<D>()), params, 0, stream);
     if (e != hipSuccess) return e;
     const unsigned dq_grid = (unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.BH);
     return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<BF16, D, CAUSAL>),
