@@ -165,31 +165,37 @@ attn_bwd_pre_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// acc[kb] += rows 32 kb .. 32 kb + 31 of `tile` (lane row lane % 32) times the
-// B-operand fragments bf over d, for kb < KB: KB * KS MFMAs whose A fragments
-// stream through a 4-deep register ring (held by scheduling groups, so each
-// LDS read is issued four fragments ahead of its use).
-template <bool BF16, int D, int KB>
-__device__ __forceinline__ void rows_times(const u16* tile, const int (&rfo)[D / 16],
-                                           const u32x4 (&bf)[D / 16], f32x16 (&acc)[KB]) {
+// LDS pointer types: fragment reads through them are a per-lane base plus an
+// immediate offset.
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) u16 lds_u16;
+
+// acc = the 32-row block at element offset `off` of the tile behind rp (rp[ks]:
+// this lane's row fragment of d step ks, lane row lane % 32) times the
+// B-operand fragments bf over d: KS MFMAs whose A fragments stream through a
+// 4-deep register ring (held by scheduling groups, so each LDS read is
+// issued four fragments ahead of its use).
+template <bool BF16, int D>
+__device__ __forceinline__ void rows_times(const lds_u32x4* const (&rp)[D / 16], int off,
+                                           const u32x4 (&bf)[D / 16], f32x16& acc) {
     using M = Mma<BF16>;
-    constexpr int KS = D / 16, NF = KB * KS;
-    auto frag = [&](int f) {
-        return *reinterpret_cast<const u32x4*>(tile + (f % KB) * 32 * D + rfo[f / KB]);
-    };
+    constexpr int KS = D / 16;
+    auto frag = [&](int f) { return rp[f][off / 8]; };
     __builtin_amdgcn_sched_barrier(0);
     u32x4 ring[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) ring[f] = frag(f);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
+    for (int f = 0; f < KS; ++f) {
         const u32x4 x = ring[f & 3];
-        if (f + 4 < NF) ring[f & 3] = frag(f + 4);
-        acc[f % KB] = M::run(x, bf[f / KB], acc[f % KB]);
+        if (f + 4 < KS) ring[f & 3] = frag(f + 4);
+        acc = M::run(x, bf[f], f == 0 ? f32x16{} : acc);
     }
     __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
 #pragma unroll
-    for (int f = 0; f < NF - 4; ++f) {
+    for (int f = 0; f < KS - 4; ++f) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
     }
@@ -198,16 +204,22 @@ __device__ __forceinline__ void rows_times(const u16* tile, const int (&rfo)[D /
 }
 
 // acc[mt] += X^T[d = 32 mt + ..][16 rows of group u] * bf[u] over the NU
-// 16-row groups of `tile`: 2 * NU * MT transpose reads through a 4-fragment
-// ring.  X^T is read in the accumulator's row order (tr_frag_offset).
+// 16-row groups of the block at element offset `off` of the tile behind tp
+// (tp[mt][r]: this lane's two transpose reads of group 0): 2 * NU * MT
+// transpose reads through a 4-fragment ring.  X^T is read in the
+// accumulator's row order (tr_frag_offset).
 template <bool BF16, int D, int NU>
-__device__ __forceinline__ void trans_times(const u16* tile, const int (&tfo)[D / 32][2],
+__device__ __forceinline__ void trans_times(const lds_s16x4* const (&tp)[D / 32][2], int off,
                                             const u32x4 (&bf)[NU], f32x16 (&acc)[D / 32]) {
     using M = Mma<BF16>;
     constexpr int MT = D / 32, NF = NU * MT;
     auto frag = [&](int f) {
-        const u16* base = tile + (f / MT) * 16 * D;
-        return tr16_b64x2(base + tfo[f % MT][0], base + tfo[f % MT][1]);
+        const int o = (off + (f / MT) * 16 * D) / 4;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp[f % MT][0] + o));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tp[f % MT][1] + o));
+        const auto lo = __builtin_bit_cast(unsigned long long, x0);
+        const auto hi = __builtin_bit_cast(unsigned long long, x1);
+        return u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi, (unsigned)(hi >> 32)};
     };
     u32x4 ring[4];
 #pragma unroll
@@ -219,6 +231,55 @@ __device__ __forceinline__ void trans_times(const u16* tile, const int (&tfo)[D 
         acc[f % MT] = M::run(x, bf[f / MT], acc[f % MT]);
     }
 }
+
+// Per-lane LDS pointers into the stage of a streamed tile: row fragments
+// (rp), transposed reads (tp) and, when the stage holds them, this lane's
+// lse2 / D entries (lp).  advance() moves them from the stage of tile fi to
+// that of tile fi + 1 (kBwdStages stages of `stage` elements).
+template <int D, bool LP>
+struct StagePtrs {
+    const lds_u32x4* rp[D / 16];
+    const lds_s16x4* tp[D / 32][2];
+    const lds_f32x4* lp;
+    __device__ __forceinline__ void init(const u16* lds, int lane, int lp_off) {
+        const int col = lane & 31;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            rp[ks] = (const lds_u32x4*)((const lds_u16*)lds + row_frag_offset<D>(col, ks, lane));
+            asm volatile("" : "+v"(rp[ks]));
+        }
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                tp[mt][r] = (const lds_s16x4*)((const lds_u16*)lds + tr_frag_offset<D>(lane, mt, r));
+                asm volatile("" : "+v"(tp[mt][r]));
+            }
+        if constexpr (LP) {
+            lp = (const lds_f32x4*)((const lds_u16*)lds + lp_off) + (lane >> 5);
+            asm volatile("" : "+v"(lp));
+        }
+    }
+    __device__ __forceinline__ void advance(int fi, int stage) {
+        const int delta = (fi % kBwdStages == kBwdStages - 1) ? -(kBwdStages - 1) * stage : stage;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            rp[ks] = (const lds_u32x4*)((const lds_u16*)rp[ks] + delta);
+            asm volatile("" : "+v"(rp[ks]));
+        }
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                tp[mt][r] = (const lds_s16x4*)((const lds_u16*)tp[mt][r] + delta);
+                asm volatile("" : "+v"(tp[mt][r]));
+            }
+        if constexpr (LP) {
+            lp = (const lds_f32x4*)((const lds_u16*)lp + delta);
+            asm volatile("" : "+v"(lp));
+        }
+    }
+};
 
 template <bool BF16, int D, bool CAUSAL>
 __global__ void __launch_bounds__(64 * dkdv_waves<D>(), 1)
@@ -263,14 +324,8 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
         dk_acc[mt] = f32x16{};
         dv_acc[mt] = f32x16{};
     }
-    int rfo[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) rfo[ks] = row_frag_offset<D>(col, ks, lane);
-    int tfo[MT][2];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 2; ++r) tfo[mt][r] = tr_frag_offset<D>(lane, mt, r);
+    StagePtrs<D, true> sp;
+    sp.init(lds, lane, 2 * TILE);
 
     // Query tiles: with causal masking only rows at or after the workgroup's
     // first key contribute.
@@ -314,14 +369,10 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     // P from the saved LSE, dS = P (dP - D), then dV^T += dO^T P and
     // dK^T += Q^T dS.  MASKED zeroes P where key > query (causal) or the
     // query row is past N.
-    auto block = [&](const u16* st, int b, int qb, auto masked_tag) {
-        const u16* qt = st + 32 * b * D;
-        const u16* dot = st + TILE + 32 * b * D;
-        const float* l2t = reinterpret_cast<const float*>(st + 2 * TILE) + 32 * b;
-        const float* ddt = l2t + kBwdTile;
-        f32x16 s[1] = {f32x16{}}, dp[1] = {f32x16{}};
-        rows_times<BF16, D, 1>(qt, rfo, kf, s);
-        rows_times<BF16, D, 1>(dot, rfo, vf, dp);
+    auto block = [&](int b, int qb, auto masked_tag) {
+        f32x16 s[1], dp[1];
+        rows_times<BF16, D>(sp.rp, 32 * b * D, kf, s[0]);
+        rows_times<BF16, D>(sp.rp, TILE + 32 * b * D, vf, dp[0]);
         int lo = 0, hi = 32;
         if constexpr (decltype(masked_tag)::value) {
             // masked iff offset e' = 8(e/4) + e%4 is < key - qb - 4g (causal)
@@ -336,8 +387,8 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int j4 = 2 * u + h;
-                const f32x4 l2 = *reinterpret_cast<const f32x4*>(l2t + 8 * j4 + 4 * g);
-                const f32x4 dd = *reinterpret_cast<const f32x4*>(ddt + 8 * j4 + 4 * g);
+                const f32x4 l2 = sp.lp[(32 * b + 8 * j4) / 4];
+                const f32x4 dd = sp.lp[(kBwdTile + 32 * b + 8 * j4) / 4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int e = 4 * j4 + i;
@@ -355,8 +406,8 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
             dsf[u] = u32x4{M::pack(ds[0], ds[1]), M::pack(ds[2], ds[3]), M::pack(ds[4], ds[5]),
                            M::pack(ds[6], ds[7])};
         }
-        trans_times<BF16, D, 2>(dot, tfo, pf, dv_acc);
-        trans_times<BF16, D, 2>(qt, tfo, dsf, dk_acc);
+        trans_times<BF16, D, 2>(sp.tp, TILE + 32 * b * D, pf, dv_acc);
+        trans_times<BF16, D, 2>(sp.tp, 32 * b * D, dsf, dk_acc);
     };
     std::integral_constant<bool, false> plain;
     std::integral_constant<bool, true> masked;
@@ -376,17 +427,17 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     for (int fi = 0; fi < nflat; ++fi) {
         issue(fi + 2);
         const int it = qt0 + fi % nt;
-        const u16* st = stage(fi);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int qb = it * kBwdTile + 32 * b;  // first query row of the block
             if (qb >= N || (CAUSAL && qb + 31 < kw)) continue;
             if ((CAUSAL && qb < kw + 31) || qb + 32 > N)
-                block(st, b, qb, masked);
+                block(b, qb, masked);
             else
-                block(st, b, qb, plain);
+                block(b, qb, plain);
         }
         wait_next(fi);
+        sp.advance(fi, STAGE);
     }
 
     // Lane (col, g) holds d = 32 mt + 8 (i / 4) + 4 g + i % 4 of key `key`.
@@ -443,14 +494,11 @@ attn_bwd_dq_kernel(BwdArgs a) {
     f32x16 dq_acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) dq_acc[mt] = f32x16{};
-    int rfo[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) rfo[ks] = row_frag_offset<D>(col, ks, lane);
-    int tfo[MT][2];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 2; ++r) tfo[mt][r] = tr_frag_offset<D>(lane, mt, r);
+    // Per-lane LDS pointers into the stage of the current tile (row
+    // fragments of the K tile, transposed reads of its first 16-row group);
+    // the V tile, the key half and the group are immediates.
+    StagePtrs<D, false> sp;
+    sp.init(lds, lane, 0);
 
     const int kv_end = CAUSAL ? min(t * kDqRows + kDqRows, N) : N;
     const int ntiles = (kv_end + kBwdTile - 1) / kBwdTile;
@@ -478,18 +526,15 @@ attn_bwd_dq_kernel(BwdArgs a) {
     // The tile is taken as two halves of 32 keys, to keep the live registers
     // within two waves per SIMD.
     auto tile = [&](int it, auto masked_tag) {
-        const u16* kt = stage(it);
-        const u16* vt = kt + TILE;
         const int key0 = it * kBwdTile;
         int lim = 1 << 30;
         if constexpr (decltype(masked_tag)::value)
             lim = min(CAUSAL ? row - key0 : (1 << 30), N - 1 - key0) - 4 * g;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const u16* kh = kt + 32 * half * D;
             f32x16 s[1] = {f32x16{}}, dp[1] = {f32x16{}};
-            rows_times<BF16, D, 1>(kh, rfo, qf, s);
-            rows_times<BF16, D, 1>(vt + 32 * half * D, rfo, dof, dp);
+            rows_times<BF16, D>(sp.rp, half * 32 * D, qf, s[0]);
+            rows_times<BF16, D>(sp.rp, TILE + half * 32 * D, dof, dp[0]);
             u32x4 dsf[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -507,7 +552,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
                 dsf[u] = u32x4{M::pack(ds[0], ds[1]), M::pack(ds[2], ds[3]), M::pack(ds[4], ds[5]),
                                M::pack(ds[6], ds[7])};
             }
-            trans_times<BF16, D, 2>(kh, tfo, dsf, dq_acc);
+            trans_times<BF16, D, 2>(sp.tp, half * 32 * D, dsf, dq_acc);
         }
     };
     std::integral_constant<bool, false> plain;
@@ -526,6 +571,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
         issue(it + 2);
         tile(it, plain);
         finish(it);
+        sp.advance(it, STAGE);
     }
     if (it == last) {
         issue(it + 2);
@@ -576,10 +622,6 @@ attn_bwd_dkdv_pipe_kernel(BwdArgs a) {
     constexpr int STAGE = 2 * TILE + 2 * kBwdTile * 2;  // Q, dO (16-bit), lse2, D (FP32)
     constexpr int LPM = copies_per_matrix<D, NW>();
     constexpr int NSTG = 4;  // stages: tile t read, t-1 still read by dV/dK, t+1 and t+2 in flight
-    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-    typedef __attribute__((address_space(3))) u16 lds_u16;
     __shared__ __attribute__((aligned(1024))) u16 lds[NSTG * STAGE];
 
     const int lane = threadIdx.x & 63;
@@ -860,8 +902,11 @@ hipError_t launch_bwd(BwdArgs a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     constexpr int kv_rows = 32 * dkdv_waves<D>();
     const unsigned grid = (unsigned)(((a.N + kv_rows - 1) / kv_rows) * a.BHkv);
-    const void* dkdv = D == 128 ? reinterpret_cast<const void*>(&attn_bwd_dkdv_pipe_kernel<BF16, CAUSAL>)
-                                : reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<BF16, D, CAUSAL>);
+    const void* dkdv;
+    if constexpr (D == 128)
+        dkdv = reinterpret_cast<const void*>(&attn_bwd_dkdv_pipe_kernel<BF16, CAUSAL>);
+    else
+        dkdv = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<BF16, D, CAUSAL>);
     e = hipLaunchKernel(dkdv, dim3(grid), dim3(64 * dkdv_waves<D>()), params, 0, stream);
     if (e != hipSuccess) return e;
     const unsigned dq_grid = (unsigned)(((a.N + kDqRows - 1) / kDqRows) * a.BH);
