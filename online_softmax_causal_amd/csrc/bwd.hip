@@ -532,7 +532,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
             lim = min(CAUSAL ? row - key0 : (1 << 30), N - 1 - key0) - 4 * g;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            f32x16 s[1] = {f32x16{}}, dp[1] = {f32x16{}};
+            f32x16 s[1], dp[1];
             rows_times<BF16, D>(sp.rp, half * 32 * D, qf, s[0]);
             rows_times<BF16, D>(sp.rp, TILE + half * 32 * D, dof, dp[0]);
             u32x4 dsf[2];
@@ -596,17 +596,20 @@ attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV at D = 128 as a software pipeline over 32-query blocks.  Same work,
-// layout and per-block arithmetic as attn_bwd_dkdv_kernel (one wave per SIMD,
-// 32 keys per wave with K^T and V^T resident), but the step of block j runs
-//   (a) if block j needs the mask: S_j set to -inf where key > query or the
-//       query row is past N (a wave-uniform branch once S_j is done);
-//   (b) S and dP of block j on the MFMA (16 MFMAs, the two products
+// dK/dV at D = 128 as a software pipeline over 32-query blocks.  Same layout
+// and per-block arithmetic as attn_bwd_dkdv_kernel (one wave per SIMD, 32
+// keys per wave with K^T and V^T resident), but the step of block j runs
+//   (a) S and dP of block j on the MFMA (16 MFMAs, the two products
 //       alternating, A operands through a 4-deep LDS ring);
+//   (b) if block j needs the mask: S_j set to -inf where key > query or the
+//       query row is past N (a wave-uniform branch);
 //   (c) dV^T += dO^T P and dK^T += Q^T dS of block j-1 (16 MFMAs,
 //       transposed LDS reads through a 4-deep ring), with block j's weights
 //       hosted between them: P = 2^(S scale - lse2), dS = P (dP - D), both
 //       packed to 16 bits.
+// A block wholly masked for the wave (all its rows before the wave's keys,
+// or past N) is computed with P = 0 instead of skipped, which keeps every
+// wave's step sequence the same; its dV/dK products add zeros.
 // Blocks 0 and 1 of a streamed tile are its two 32-row halves; block 0's
 // step finishes block 1 of the previous tile, so four LDS stages hold the
 // tile being read, the previous one (its last dV/dK) and two in flight.
