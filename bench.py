@@ -597,6 +597,64 @@ def ceiling(seconds=3.0, pairs=2000):
     torch.cuda.synchronize()
     rows.append(("attn_bwd " + w.describe().replace("fwd", "bwd") + " (algorithmic FLOP)",
                  measure_clock(bwd, 2.5 * w.flops, seconds)))
+    del q, k, v, do, o, lse, grads, ws
+
+    # HBM: streaming read and copy of 1 GiB, then the row softmax (R2) and the
+    # 32K-token paged decode (D32), each timed the same way (bytes per second).
+    lib.osc_hbm_read_launch.restype = ctypes.c_int
+    lib.osc_hbm_read_launch.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p]
+    lib.osc_hbm_copy_launch.restype = ctypes.c_int
+    lib.osc_hbm_copy_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_void_p]
+    nbytes = 1 << 30
+    hsrc = torch.randint(0, 1 << 30, (nbytes // 4,), dtype=torch.int32, device=dev)
+    hdst = torch.empty_like(hsrc)
+    hout = torch.empty(grid * 4 * 256, dtype=torch.int32, device=dev)
+    hbm_rows = []
+
+    def hread():  # 4 workgroups per CU
+        e = lib.osc_hbm_read_launch(hsrc.data_ptr(), nbytes, hout.data_ptr(), grid * 4, stream)
+        if e != 0:
+            raise RuntimeError("HBM read probe launch failed: %d" % e)
+
+    def hcopy():  # 2 workgroups per CU
+        e = lib.osc_hbm_copy_launch(hsrc.data_ptr(), hdst.data_ptr(), nbytes, grid * 2, stream)
+        if e != 0:
+            raise RuntimeError("HBM copy probe launch failed: %d" % e)
+    for desc, fn, moved in (("streaming read, 16-byte non-temporal loads (1 GiB)", hread, nbytes),
+                            ("streaming copy, 16-byte non-temporal loads and stores (1 GiB each way)",
+                             hcopy, 2 * nbytes)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        hbm_rows.append((desc, measure_clock(fn, moved, seconds)))
+    del hsrc, hdst, hout
+    sw = workloads.SOFTMAX["R2"]
+    x = workloads.softmax_inputs(sw.M, sw.N, seed=sw.seed, last=sw.last).to(dev)
+    y = torch.empty_like(x)
+
+    def smax():
+        osc.row_softmax(x, y, sw.M, sw.N)
+    for _ in range(5):
+        smax()
+    torch.cuda.synchronize()
+    hbm_rows.append((sw.describe() + " (read + write)", measure_clock(smax, 8.0 * sw.M * sw.N, seconds)))
+    del x, y
+    dw = workloads.DECODE["D32"]
+    dq, cache, bt, ln = (t.to(dev) for t in workloads.decode_workload_inputs(dw))
+    do_ = torch.empty((dw.B, dw.Hq, dw.D), dtype=torch.float32, device=dev)
+    dl = torch.empty((dw.B, dw.Hq), dtype=torch.float32, device=dev)
+    dneed = osc.paged_decode_workspace(dw.B, dw.Hq, dw.Hkv, dw.D, dw.page_size, dw.max_pages, 0)
+    dws = torch.empty((max(dneed, 16) // 4,), dtype=torch.float32, device=dev)
+
+    def dec():
+        osc.paged_decode(dq, cache, bt, ln, do_, dl, dw.B, dw.Hq, dw.Hkv, dw.D, dw.page_size,
+                         dw.num_pages, dw.max_pages, dw.dtype, 0, dws, dneed)
+    for _ in range(5):
+        dec()
+    torch.cuda.synchronize()
+    hbm_rows.append((dw.describe() + " (reads)", measure_clock(dec, float(dw.bytes), seconds)))
     print("sustained matrix-core rate per instruction mix: %.1f s back-to-back runs, amdsmi sampling"
           % seconds)
     print("probe grid %d workgroups x 8 waves, %d iterations of 32 MFMAs per wave per launch" % (grid, pairs))
@@ -610,8 +668,19 @@ def ceiling(seconds=3.0, pairs=2000):
             desc, c["sustained_tflops"], 100.0 * c["sustained_tflops"] / PEAK_F16_TFLOPS, c["clock_mhz"],
             c["power_w"] or float("nan"), 100.0 * c["frac_of_peak_at_clock"]))
     print("")
-    print("sources_sha256_16: ceiling.hip %s, attn_fwd.hip+mfma_tile.hpp+online_merge.hpp %s"
-          % (kernel_source_hash(("ceiling.hip",)), kernel_source_hash()))
+    print("workload | TB/s | % of 8 TB/s | GFX MHz | W")
+    for desc, c in hbm_rows:
+        if c is None:
+            print("%s | (amdsmi unavailable)" % desc)
+            continue
+        print("%s | %.2f | %.1f | %.0f | %.0f" % (
+            desc, c["sustained_tflops"], 100.0 * c["sustained_tflops"] / (PEAK_HBM_GBS / 1000.0),
+            c["clock_mhz"], c["power_w"] or float("nan")))
+    print("")
+    print("sources_sha256_16: ceiling.hip %s, attn_fwd.hip+mfma_tile.hpp+online_merge.hpp %s, "
+          "row_softmax.hip %s, decode.hip %s"
+          % (kernel_source_hash(("ceiling.hip",)), kernel_source_hash(),
+             kernel_source_hash(("row_softmax.hip",)), kernel_source_hash(("decode.hip",))))
 
 
 def _pmc_rows(path):

@@ -20,6 +20,13 @@
 //   mix 3  mix 1 plus that work on two values per MFMA and one pack per MFMA
 //          (the score density at D = 64: 64 scores per lane per 32 MFMAs).
 // bench.py runs each mix back to back while sampling clock and power.
+//
+// Two HBM probes give the same kind of reference for the memory-bound paths:
+// a streaming read and a streaming copy, both grid-stride with 16-byte
+// non-temporal accesses.  Their shapes are the fastest of a sweep over grid
+// size, accesses in flight per thread and temporal / non-temporal accesses:
+// the read with 4 workgroups per CU and 8 loads in flight per thread (6.6
+// TB/s), the copy with 2 workgroups per CU and 4 (5.7 TB/s read + write).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -29,6 +36,7 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
 constexpr int kLdsVec = 6144;  // 96 KiB of 16-byte vectors: one workgroup per CU
@@ -108,6 +116,49 @@ ceiling_kernel(const f16x8* __restrict__ src, float* __restrict__ out, int pairs
     out[(int64_t)blockIdx.x * kThreads + tid] = r;
 }
 
+constexpr int kHbmThreads = 256;
+
+constexpr int kReadInFlight = 8;   // loads per thread per round
+constexpr int kCopyInFlight = 4;
+
+// Reads n16 16-byte vectors of src; thread t stores the XOR of what it read.
+__global__ void __launch_bounds__(kHbmThreads)
+hbm_read_kernel(const u32x4* __restrict__ src, int64_t n16, unsigned* __restrict__ out) {
+    constexpr int U = kReadInFlight;
+    const int64_t t = (int64_t)blockIdx.x * kHbmThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kHbmThreads;
+    u32x4 a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = u32x4{0u, 0u, 0u, 0u};
+    int64_t i = t;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] ^= __builtin_nontemporal_load(src + i + u * stride);
+    }
+    for (; i < n16; i += stride) a[0] ^= __builtin_nontemporal_load(src + i);
+    unsigned r = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) r ^= a[u][0] ^ a[u][1] ^ a[u][2] ^ a[u][3];
+    out[t] = r;
+}
+
+// Copies n16 16-byte vectors from src to dst.
+__global__ void __launch_bounds__(kHbmThreads)
+hbm_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n16) {
+    constexpr int U = kCopyInFlight;
+    const int64_t t = (int64_t)blockIdx.x * kHbmThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kHbmThreads;
+    int64_t i = t;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u32x4 a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(a[u], dst + i + u * stride);
+    }
+    for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +182,31 @@ int osc_ceiling_launch(int mix, const void* src, float* out, int grid, int iters
                    : mix == 2 ? reinterpret_cast<const void*>(&ceiling_kernel<2>)
                               : reinterpret_cast<const void*>(&ceiling_kernel<3>);
     return (int)hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
+}
+
+// Streaming read of `bytes` (a multiple of 16) from src: `grid` workgroups of
+// 256 threads; out: device buffer of grid * 256 unsigned.  Returns a
+// hipError_t value (hipErrorInvalidValue for a bad argument, nothing
+// enqueued).
+int osc_hbm_read_launch(const void* src, int64_t bytes, unsigned* out, int grid, hipStream_t stream) {
+    if (!src || !out || bytes < 16 || bytes % 16 != 0 || grid < 1) return (int)hipErrorInvalidValue;
+    const u32x4* s = static_cast<const u32x4*>(src);
+    int64_t n16 = bytes / 16;
+    void* params[] = {(void*)&s, (void*)&n16, (void*)&out};
+    return (int)hipLaunchKernel(reinterpret_cast<const void*>(&hbm_read_kernel), dim3((unsigned)grid),
+                                dim3(kHbmThreads), params, 0, stream);
+}
+
+// Streaming copy of `bytes` (a multiple of 16) from src to dst (which must not
+// overlap): `grid` workgroups of 256 threads.  Returns as osc_hbm_read_launch.
+int osc_hbm_copy_launch(const void* src, void* dst, int64_t bytes, int grid, hipStream_t stream) {
+    if (!src || !dst || bytes < 16 || bytes % 16 != 0 || grid < 1) return (int)hipErrorInvalidValue;
+    const u32x4* s = static_cast<const u32x4*>(src);
+    u32x4* d = static_cast<u32x4*>(dst);
+    int64_t n16 = bytes / 16;
+    void* params[] = {(void*)&s, (void*)&d, (void*)&n16};
+    return (int)hipLaunchKernel(reinterpret_cast<const void*>(&hbm_copy_kernel), dim3((unsigned)grid),
+                                dim3(kHbmThreads), params, 0, stream);
 }
 
 }  // extern "C"
