@@ -154,8 +154,11 @@ paged_decode_kernel(DecodeArgs a) {
             const int pid = page_ids[(t >> lp) - p0];
             const int64_t row = ((int64_t)pid * 2 * T + (t & (T - 1))) * a.Hkv + kvh;
             const u16* src = a.cache + row * D + c * 8;
-            copy_to_lds16_at(src, kd + j * 512);
-            copy_to_lds16_at(src + kv_stride, kd + TILE + j * 512);
+            // Each cached row is read by one workgroup once per call: the
+            // copies carry the non-temporal hint, so the stream does not
+            // displace reusable lines from the caches.
+            copy_to_lds16_at_nt(src, kd + j * 512);
+            copy_to_lds16_at_nt(src + kv_stride, kd + TILE + j * 512);
         }
     };
 

@@ -169,6 +169,14 @@ __device__ __forceinline__ void copy_to_lds16_at(const void* gaddr, void* lds_ds
                  : "m0");
 }
 
+// The same with the non-temporal hint, for data read exactly once.
+__device__ __forceinline__ void copy_to_lds16_at_nt(const void* gaddr, void* lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :
+                 : "s"(lds_offset(lds_dst)), "v"(gaddr)
+                 : "m0");
+}
+
 // Wait until at most `n` of this wave's vector-memory loads are outstanding
 // (gfx9 s_waitcnt encoding; expcnt and lgkmcnt are left at their maxima so they
 // are not waited on).

@@ -29,10 +29,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Quads are 16-byte aligned groups of 4 floats.  A row that starts `off`
 // floats past a 16-byte boundary covers quads 0 .. nq-1 of the aligned base
 // pointer pb = row - off; quad j holds row elements 4j - off + t, t = 0..3.
+// NT: the kernels that keep the row in registers read x and write y exactly
+// once, so their whole quads carry the non-temporal hint; the streaming
+// kernel reads each row twice and keeps the default policy.
+template <bool NT>
 __device__ __forceinline__ void load_quad(const float* pb, int off, int n, int j, float (&v)[4]) {
     const int e0 = 4 * j - off;
     if (e0 >= 0 && e0 + 3 < n) {
-        const f32x4 q = *reinterpret_cast<const f32x4*>(pb + 4 * j);
+        const f32x4* p = reinterpret_cast<const f32x4*>(pb + 4 * j);
+        const f32x4 q = NT ? __builtin_nontemporal_load(p) : *p;
         v[0] = q[0];
         v[1] = q[1];
         v[2] = q[2];
@@ -48,11 +53,16 @@ __device__ __forceinline__ void load_quad(const float* pb, int off, int n, int j
 
 // Store the elements of quad j (x-aligned numbering) into the y row.  When y
 // has the same 16-byte phase as x the quad maps onto one aligned y quad.
+template <bool NT>
 __device__ __forceinline__ void store_quad(float* yrow, int xoff, bool same_phase, int n, int j,
                                            const float (&v)[4]) {
     const int e0 = 4 * j - xoff;
     if (same_phase && e0 >= 0 && e0 + 3 < n) {
-        *reinterpret_cast<f32x4*>(yrow + e0) = f32x4{v[0], v[1], v[2], v[3]};
+        const f32x4 q = {v[0], v[1], v[2], v[3]};
+        if constexpr (NT)
+            __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(yrow + e0));
+        else
+            *reinterpret_cast<f32x4*>(yrow + e0) = q;
     } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -107,7 +117,7 @@ softmax_wave_rows(const float* __restrict__ x, float* __restrict__ y, int M, int
     for (int it = 0; it < ITEMS; ++it) {
         const int j = lane + 64 * it;
         if (j < nq) {
-            load_quad(pb, off, N, j, v[it]);
+            load_quad<true>(pb, off, N, j, v[it]);
         } else {
 #pragma unroll
             for (int t = 0; t < 4; ++t) v[it][t] = -INFINITY;
@@ -123,7 +133,7 @@ softmax_wave_rows(const float* __restrict__ x, float* __restrict__ y, int M, int
             float r[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) r[t] = v[it][t] * f;
-            store_quad(yrow, off, same, N, j, r);
+            store_quad<true>(yrow, off, same, N, j, r);
         }
     }
 }
@@ -166,7 +176,7 @@ softmax_block_row(const float* __restrict__ x, float* __restrict__ y, int N) {
     for (int it = 0; it < ITEMS; ++it) {
         const int j = threadIdx.x + kBlockThreads * it;
         if (j < nq) {
-            load_quad(pb, off, N, j, v[it]);
+            load_quad<true>(pb, off, N, j, v[it]);
         } else {
 #pragma unroll
             for (int t = 0; t < 4; ++t) v[it][t] = -INFINITY;
@@ -182,7 +192,7 @@ softmax_block_row(const float* __restrict__ x, float* __restrict__ y, int N) {
             float r[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) r[t] = v[it][t] * f;
-            store_quad(yrow, off, same, N, j, r);
+            store_quad<true>(yrow, off, same, N, j, r);
         }
     }
 }
@@ -203,7 +213,7 @@ softmax_block_row_stream(const float* __restrict__ x, float* __restrict__ y, int
     OnlineState s{-INFINITY, 0.0f};
     for (int j = threadIdx.x; j < nq; j += kBlockThreads) {
         float v[4];
-        load_quad(pb, off, N, j, v);
+        load_quad<false>(pb, off, N, j, v);
         const float qmax = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
         const float m_new = fmaxf(s.m, qmax * kLog2e);
         const float pivot = online_pivot(m_new);
@@ -217,10 +227,10 @@ softmax_block_row_stream(const float* __restrict__ x, float* __restrict__ y, int
     const float inv = 1.0f / row_state.l;
     for (int j = threadIdx.x; j < nq; j += kBlockThreads) {
         float v[4];
-        load_quad(pb, off, N, j, v);
+        load_quad<false>(pb, off, N, j, v);
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = fast_exp2(fmaf(v[t], kLog2e, -row_state.m)) * inv;
-        store_quad(yrow, off, same, N, j, v);
+        store_quad<false>(yrow, off, same, N, j, v);
     }
 }
 
