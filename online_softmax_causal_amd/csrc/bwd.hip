@@ -600,7 +600,8 @@ attn_bwd_dq_kernel(BwdArgs a) {
 // and per-block arithmetic as attn_bwd_dkdv_kernel (one wave per SIMD, 32
 // keys per wave with K^T and V^T resident), but the step of block j runs
 //   (a) S and dP of block j on the MFMA (16 MFMAs, the two products
-//       alternating, A operands through a 4-deep LDS ring);
+//       alternating, A operands through a 4-deep LDS ring that runs on
+//       across the steps of a tile);
 //   (b) if block j needs the mask: S_j set to -inf where key > query or the
 //       query row is past N (a wave-uniform branch);
 //   (c) dV^T += dO^T P and dK^T += Q^T dS of block j-1 (16 MFMAs,
@@ -750,16 +751,35 @@ attn_bwd_dkdv_pipe_kernel(BwdArgs a) {
     u32x4 pf0[2], dsf0[2], pf1[2], dsf1[2];  // packed P, dS of even / odd blocks
     u32x4 ring[4];
 
+    // Operand streams of the two kinds of step, as functions of the fragment
+    // index: row fragments of block b (products) and transposed fragments of
+    // block pb (dV/dK).  A step given WARM finds its first four fragments
+    // already in the ring; a step given a `next` stream reads that stream's
+    // first four fragments into the slots its last four MFMAs free, so the
+    // ring runs on from step to step within a tile.
+    auto rhead = [&](int b) __attribute__((always_inline)) {
+        return [&, b](int j) __attribute__((always_inline)) { return rfrag(j & 1, b, j >> 1); };
+    };
+    auto thead = [&](int pb) __attribute__((always_inline)) {
+        return [&, pb](int j) __attribute__((always_inline)) {
+            return tfrag(1 - (j & 1), pb, (j >> 1) / MT, (j >> 1) % MT);
+        };
+    };
     // S and dP of block b of the tile behind rp: fragment f is the S product
     // (ks = f/2) for even f, the dP product for odd f.
-    auto products = [&](int b) __attribute__((always_inline)) {
+    auto products = [&](int b, auto warm_c, auto next) __attribute__((always_inline)) {
+        constexpr bool WARM = decltype(warm_c)::value;
+        constexpr bool NEXT = !std::is_same_v<decltype(next), std::nullptr_t>;
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!WARM) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) ring[f] = rfrag(f & 1, b, f >> 1);
+            for (int f = 0; f < 4; ++f) ring[f] = rfrag(f & 1, b, f >> 1);
+        }
 #pragma unroll
         for (int f = 0; f < 2 * KS; ++f) {
             const u32x4 x = ring[f & 3];
             if (f + 4 < 2 * KS) ring[f & 3] = rfrag((f + 4) & 1, b, (f + 4) >> 1);
+            else if constexpr (NEXT) ring[f & 3] = next(f + 4 - 2 * KS);
             if (f & 1)
                 dpc = M::run(x, vf[f >> 1], f < 2 ? f32x16{} : dpc);
             else
@@ -773,8 +793,10 @@ attn_bwd_dkdv_pipe_kernel(BwdArgs a) {
     // dsfp): fragment f is dV (even) or dK (odd) of pair (u, mt) =
     // ((f/2) / MT, (f/2) % MT); element e of the weights runs after MFMA e.
     auto weights = [&](auto prev_c, int b, int qb, u32x4 (&pf)[2], u32x4 (&dsf)[2], int pb,
-                       const u32x4 (&pfp)[2], const u32x4 (&dsfp)[2]) __attribute__((always_inline)) {
+                       const u32x4 (&pfp)[2], const u32x4 (&dsfp)[2], auto warm_c, auto next) __attribute__((always_inline)) {
         constexpr bool PREV = decltype(prev_c)::value;
+        constexpr bool WARM = decltype(warm_c)::value;
+        constexpr bool NEXT = !std::is_same_v<decltype(next), std::nullptr_t>;
         if (needs_mask(qb)) mask_s(sc, qb);
         float p[16], ds[16];
         f32x4 l2, dd;
@@ -798,13 +820,16 @@ attn_bwd_dkdv_pipe_kernel(BwdArgs a) {
         };
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (PREV) {
+            if constexpr (!WARM) {
 #pragma unroll
-            for (int f = 0; f < 4; ++f) ring[f] = tfrag(1 - (f & 1), pb, (f >> 1) / MT, (f >> 1) % MT);
+                for (int f = 0; f < 4; ++f) ring[f] = tfrag(1 - (f & 1), pb, (f >> 1) / MT, (f >> 1) % MT);
+            }
 #pragma unroll
             for (int f = 0; f < 4 * MT; ++f) {
                 const u32x4 x = ring[f & 3];
                 const int nf = f + 4;
                 if (nf < 4 * MT) ring[f & 3] = tfrag(1 - (nf & 1), pb, (nf >> 1) / MT, (nf >> 1) % MT);
+                else if constexpr (NEXT) ring[f & 3] = next(nf - 4 * MT);
                 const int u = (f >> 1) / MT, mt = (f >> 1) % MT;
                 if (f & 1)
                     dk_acc[mt] = M::run(x, dsfp[u], dk_acc[mt]);
@@ -837,6 +862,8 @@ attn_bwd_dkdv_pipe_kernel(BwdArgs a) {
     };
     std::integral_constant<bool, true> prev;
     std::integral_constant<bool, false> none;
+    std::integral_constant<bool, true> warm;
+    std::integral_constant<bool, false> cold;
 
     // Tile fi complete for all waves, tile fi+1's copies (if any) still in
     // flight; then the copies of tile fi+2 into the stage of tile fi-2,
@@ -861,19 +888,21 @@ attn_bwd_dkdv_pipe_kernel(BwdArgs a) {
     rebase_trans(0);
     // Tile 0: block 0 has no predecessor.
     int qb = tile_row0(0);
-    products(0);
-    weights(none, 0, qb, pf0, dsf0, 0, pf1, dsf1);
-    products(1);
-    weights(prev, 1, qb + 32, pf1, dsf1, 0, pf0, dsf0);
+    products(0, cold, nullptr);
+    weights(none, 0, qb, pf0, dsf0, 0, pf1, dsf1, cold, nullptr);
+    products(1, cold, thead(0));
+    weights(prev, 1, qb + 32, pf1, dsf1, 0, pf0, dsf0, warm, nullptr);
     for (int fi = 1; fi < nflat; ++fi) {
         arrive(fi);
         rebase_rows(fi);
         qb = tile_row0(fi);
-        products(0);
-        weights(prev, 0, qb, pf0, dsf0, 1, pf1, dsf1);   // dV/dK of block 1 of tile fi-1
+        // Within the tile each step's last MFMAs read the next step's first
+        // fragments (the barrier of arrive() separates the tiles).
+        products(0, cold, thead(1));
+        weights(prev, 0, qb, pf0, dsf0, 1, pf1, dsf1, warm, rhead(1));   // dV/dK of block 1 of tile fi-1
         rebase_trans(fi);
-        products(1);
-        weights(prev, 1, qb + 32, pf1, dsf1, 0, pf0, dsf0);
+        products(1, warm, thead(0));
+        weights(prev, 1, qb + 32, pf1, dsf1, 0, pf0, dsf0, warm, nullptr);
     }
     finish(1, pf1, dsf1);
 
