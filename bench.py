@@ -530,8 +530,10 @@ def profile_bwd(launches=10):
 
 
 def ceiling(seconds=3.0, pairs=2000):
-    """Sustained TFLOP/s, clock and power of the ceiling probe's three mixes
-    and of attn_fwd on C4, one after the other in this process."""
+    """Sustained TFLOP/s, clock and power of the ceiling probe's six mixes,
+    of attn_fwd on C4 and C5 and attn_bwd on C4, then the HBM probes beside
+    row_softmax (R2) and paged_decode (D32), one after the other in this
+    process."""
     import ctypes
     import torch
     import online_softmax_causal_amd as osc
@@ -542,6 +544,7 @@ def ceiling(seconds=3.0, pairs=2000):
     lib = ctypes.CDLL(path)
     lib.osc_ceiling_src_bytes.restype = ctypes.c_int64
     lib.osc_ceiling_mfma_per_wg_iter.restype = ctypes.c_int
+    lib.osc_ceiling_mfma_per_wg_iter.argtypes = [ctypes.c_int]
     lib.osc_ceiling_launch.restype = ctypes.c_int
     lib.osc_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_void_p]
@@ -551,14 +554,16 @@ def ceiling(seconds=3.0, pairs=2000):
     src = (torch.rand(n16, generator=gen) * 4.0 - 2.0).to(torch.float16).to(dev)
     grid = torch.cuda.get_device_properties(dev).multi_processor_count
     out = torch.empty(grid * 512, dtype=torch.float32, device=dev)
-    flops = float(grid) * lib.osc_ceiling_mfma_per_wg_iter() * pairs * 32768.0
     stream = torch.cuda.current_stream().cuda_stream
     mixes = ((0, "MFMA only (v_mfma_f32_32x32x16_f16, random fp16 operands)"),
              (1, "MFMA + one 1 KiB LDS fragment read per MFMA per wave"),
              (2, "MFMA + LDS read + fma, exp2, add, 1/2 fp16 pack per MFMA"),
-             (3, "MFMA + LDS read + 2 x (fma, exp2, add), 1 fp16 pack per MFMA"))
+             (3, "MFMA + LDS read + 2 x (fma, exp2, add), 1 fp16 pack per MFMA"),
+             (4, "mix 2 at one wave per SIMD"),
+             (5, "mix 2 at one wave per SIMD, each LDS fragment feeding two MFMAs"))
     rows = []
     for mix, desc in mixes:
+        flops = float(grid) * lib.osc_ceiling_mfma_per_wg_iter(mix) * pairs * 32768.0
         def step(mix=mix):
             e = lib.osc_ceiling_launch(mix, src.data_ptr(), out.data_ptr(), grid, pairs, stream)
             if e != 0:
@@ -657,7 +662,8 @@ def ceiling(seconds=3.0, pairs=2000):
     hbm_rows.append((dw.describe() + " (reads)", measure_clock(dec, float(dw.bytes), seconds)))
     print("sustained matrix-core rate per instruction mix: %.1f s back-to-back runs, amdsmi sampling"
           % seconds)
-    print("probe grid %d workgroups x 8 waves, %d iterations of 32 MFMAs per wave per launch" % (grid, pairs))
+    print("probe grid %d workgroups x 8 waves (4 for mixes 4 and 5), %d iterations of 32 MFMAs per wave per launch"
+          % (grid, pairs))
     print("")
     print("workload | TFLOP/s | % of 2516.6 | GFX MHz | W | % of peak at that clock")
     for desc, c in rows:

@@ -18,7 +18,11 @@
 //          (the forward kernel's per-score softmax work at D = 128: 32 scores
 //          per lane per 32 MFMAs);
 //   mix 3  mix 1 plus that work on two values per MFMA and one pack per MFMA
-//          (the score density at D = 64: 64 scores per lane per 32 MFMAs).
+//          (the score density at D = 64: 64 scores per lane per 32 MFMAs);
+//   mix 4  mix 2 with one wave per SIMD (256-thread workgroups);
+//   mix 5  mix 4 with each LDS fragment feeding two MFMAs (two B operands,
+//          as a wave holding two 32-row query blocks would): half the LDS
+//          reads per MFMA, the same softmax work per MFMA.
 // bench.py runs each mix back to back while sampling clock and power.
 //
 // Two HBM probes give the same kind of reference for the memory-bound paths:
@@ -38,25 +42,35 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
 constexpr int kLdsVec = 6144;  // 96 KiB of 16-byte vectors: one workgroup per CU
 constexpr int kMfmaPerIter = 16;
 
-// One step: 16 MFMAs into accumulator set PH; with MIX >= 1 each takes its A
-// operand from a ring of 4 LDS fragments read 4 MFMAs ahead; with MIX = 2 the
-// VALU work reads set PH ^ 1, written by the previous step (so it never waits
-// on an MFMA in flight, as the softmax of a finished tile does not).
+// Threads per workgroup: two waves per SIMD, or one for mixes 4 and 5.
+constexpr int threads_of(int mix) { return mix >= 4 ? 256 : 512; }
+
+// One step: 16 MFMAs into accumulator set PH; with MIX >= 1 their A operands
+// come from a ring of 4 LDS fragments, each read 4 fragments ahead of its
+// use and used by QB consecutive MFMAs (QB = 2 for mix 5, with B operands
+// b0 and b1 alternating); with MIX >= 2 the VALU work reads set PH ^ 1,
+// written by the previous step (so it never waits on an MFMA in flight, as
+// the softmax of a finished tile does not).
 template <int MIX, int PH>
 __device__ __forceinline__ void ceiling_step(f32x16 (&c)[2][4], f16x8 (&ring)[4], const f16x8& a,
-                                             const f16x8& b, const f16x8 __attribute__((address_space(3)))* base,
+                                             const f16x8& b0, const f16x8& b1,
+                                             const f16x8 __attribute__((address_space(3)))* base,
                                              float& sum, float& p0) {
+    constexpr int QB = MIX == 5 ? 2 : 1;
 #pragma unroll
     for (int m = 0; m < kMfmaPerIter; ++m) {
-        const f16x8 av = MIX >= 1 ? ring[m & 3] : a;
-        c[PH][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b, c[PH][m & 3], 0, 0, 0);
-        if constexpr (MIX >= 1) ring[m & 3] = base[256 * ((m + 4) & 15)];
-        // Values per MFMA: 1 (mix 2) or 2 (mix 3); a pack per two values.
-        constexpr int VPM = MIX == 2 ? 1 : MIX == 3 ? 2 : 0;
+        const int fi = m / QB;
+        const f16x8 av = MIX >= 1 ? ring[fi & 3] : a;
+        const f16x8 bv = (QB == 2 && (m & 1)) ? b1 : b0;
+        c[PH][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, c[PH][m & 3], 0, 0, 0);
+        if constexpr (MIX >= 1) {
+            if (m % QB == QB - 1) ring[fi & 3] = base[256 * ((fi + 4) & 15)];
+        }
+        // Values per MFMA: 1 (mixes 2, 4, 5) or 2 (mix 3); a pack per two values.
+        constexpr int VPM = MIX == 3 ? 2 : MIX >= 2 ? 1 : 0;
 #pragma unroll
         for (int v = 0; v < VPM; ++v) {
             const int x = m * VPM + v;  // < 32: chains 0 and 1 of the other set
@@ -76,22 +90,25 @@ __device__ __forceinline__ void ceiling_step(f32x16 (&c)[2][4], f16x8 (&ring)[4]
 }
 
 template <int MIX>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(threads_of(MIX), 1)
 ceiling_kernel(const f16x8* __restrict__ src, float* __restrict__ out, int pairs) {
     typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
+    constexpr int NT = threads_of(MIX);
     __shared__ f16x8 lds[kLdsVec];
     const int tid = threadIdx.x;
-    for (int i = tid; i < kLdsVec; i += kThreads) lds[i] = src[i];
+    for (int i = tid; i < kLdsVec; i += NT) lds[i] = src[i];
     __syncthreads();
+    // Operands from the first 2048 vectors of src (tid < 512).
     const f16x8 a = src[tid];
-    const f16x8 b = src[kThreads + tid];
+    const f16x8 b0 = src[512 + tid];
+    const f16x8 b1 = src[1536 + tid];
     f32x16 c[2][4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) c[h][j][e] = (float)src[2 * kThreads + tid][(e + j + h) & 7];
+            for (int e = 0; e < 16; ++e) c[h][j][e] = (float)src[1024 + tid][(e + j + h) & 7];
     float sum = 0.0f, p0 = 0.0f;
     // Lane reads base[256 m], m < 16: vectors below 511 + 3840 < kLdsVec.
     const lds_f16x8* base = (const lds_f16x8*)lds + tid;
@@ -101,8 +118,8 @@ ceiling_kernel(const f16x8* __restrict__ src, float* __restrict__ out, int pairs
     for (int it = 0; it < pairs; ++it) {
         // Opaque per iteration, so the LDS reads are not hoisted out of the loop.
         asm volatile("" : "+v"(base));
-        ceiling_step<MIX, 0>(c, ring, a, b, base, sum, p0);
-        ceiling_step<MIX, 1>(c, ring, a, b, base, sum, p0);
+        ceiling_step<MIX, 0>(c, ring, a, b0, b1, base, sum, p0);
+        ceiling_step<MIX, 1>(c, ring, a, b0, b1, base, sum, p0);
     }
     float r = sum;
 #pragma unroll
@@ -113,7 +130,7 @@ ceiling_kernel(const f16x8* __restrict__ src, float* __restrict__ out, int pairs
             for (int e = 0; e < 16; ++e) r += c[h][j][e];
 #pragma unroll
     for (int q = 0; q < 4; ++q) r += (float)ring[q][q];
-    out[(int64_t)blockIdx.x * kThreads + tid] = r;
+    out[(int64_t)blockIdx.x * 512 + tid] = r;
 }
 
 constexpr int kHbmThreads = 256;
@@ -166,22 +183,29 @@ extern "C" {
 // Bytes of fp16 source data the probe reads (random values, caller-filled).
 int64_t osc_ceiling_src_bytes() { return (int64_t)kLdsVec * 16; }
 
-// MFMAs one launch issues per workgroup and iteration (x 32768 FLOP each).
-int osc_ceiling_mfma_per_wg_iter() { return (kThreads / 64) * 2 * kMfmaPerIter; }
+// MFMAs one launch of mix `mix` issues per workgroup and iteration (x 32768
+// FLOP each); 0 for a mix outside 0 to 5.
+int osc_ceiling_mfma_per_wg_iter(int mix) {
+    if (mix < 0 || mix > 5) return 0;
+    return (threads_of(mix) / 64) * 2 * kMfmaPerIter;
+}
 
-// Enqueue one launch of mix `mix` (0 to 3) on `stream`: `grid` workgroups of
-// `iters` iterations (of 2 x 16 MFMAs per wave) each.  src: device buffer of osc_ceiling_src_bytes()
-// bytes; out: device buffer of grid * 512 floats.  Returns a hipError_t
-// value (hipErrorInvalidValue for a bad argument, nothing enqueued).
+// Enqueue one launch of mix `mix` (0 to 5) on `stream`: `grid` workgroups of
+// `iters` iterations (of 2 x 16 MFMAs per wave) each.  src: device buffer of
+// osc_ceiling_src_bytes() bytes; out: device buffer of grid * 512 floats.
+// Returns a hipError_t value (hipErrorInvalidValue for a bad argument,
+// nothing enqueued).
 int osc_ceiling_launch(int mix, const void* src, float* out, int grid, int iters, hipStream_t stream) {
-    if (!src || !out || grid < 1 || iters < 1 || mix < 0 || mix > 3) return (int)hipErrorInvalidValue;
+    if (!src || !out || grid < 1 || iters < 1 || mix < 0 || mix > 5) return (int)hipErrorInvalidValue;
     const f16x8* s = static_cast<const f16x8*>(src);
     void* params[] = {(void*)&s, (void*)&out, (void*)&iters};
-    const void* fn = mix == 0   ? reinterpret_cast<const void*>(&ceiling_kernel<0>)
-                   : mix == 1 ? reinterpret_cast<const void*>(&ceiling_kernel<1>)
-                   : mix == 2 ? reinterpret_cast<const void*>(&ceiling_kernel<2>)
-                              : reinterpret_cast<const void*>(&ceiling_kernel<3>);
-    return (int)hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), params, 0, stream);
+    const void* fns[] = {reinterpret_cast<const void*>(&ceiling_kernel<0>),
+                         reinterpret_cast<const void*>(&ceiling_kernel<1>),
+                         reinterpret_cast<const void*>(&ceiling_kernel<2>),
+                         reinterpret_cast<const void*>(&ceiling_kernel<3>),
+                         reinterpret_cast<const void*>(&ceiling_kernel<4>),
+                         reinterpret_cast<const void*>(&ceiling_kernel<5>)};
+    return (int)hipLaunchKernel(fns[mix], dim3((unsigned)grid), dim3(threads_of(mix)), params, 0, stream);
 }
 
 // Streaming read of `bytes` (a multiple of 16) from src: `grid` workgroups of
