@@ -710,8 +710,9 @@ def _per_dispatch(rows, counter, match):
 
 def is_fwd_kernel(name: str) -> bool:
     """The attention forward kernels (8-wave pipeline kernel at D = 128, 8-wave unit kernel at
-    D = 64, 4-wave ring kernel)."""
-    return "attn_fwd_pipe_kernel" in name or "attn_fwd_units_kernel" in name or "attn_fwd_kernel" in name
+    D = 64, 4-wave ring kernel, key-split kernel)."""
+    return any(k in name for k in ("attn_fwd_pipe_kernel", "attn_fwd_units_kernel", "attn_fwd_kernel",
+                                   "attn_fwd_ksplit_kernel"))
 
 
 def traffic_path(name):
