@@ -10,10 +10,13 @@ ATTN_LSE = 1e-3
 SOFTMAX_Y = 1e-6
 SOFTMAX_ROWSUM = 1e-5
 
-# Attention backward (no tolerance is given for it; derived from the
-# arithmetic): P and dS are rounded to the input dtype (unit roundoff u =
-# 2^-11 for fp16, 2^-8 for bf16) before the FP32-accumulated products, which
-# perturbs each term of the dV, dK and dQ contractions by at most about 2u
-# relative; allowing the absolute-term sums to exceed the largest gradient
-# entry by a factor 2 gives max |G - G_ref| <= 4u * max(1, max |G_ref|).
+# Attention backward: no tolerance is given for it, so this is an empirical
+# margin, not a derived bound.  What the arithmetic fixes: P and dS are
+# rounded to the input dtype (unit roundoff u = 2^-11 for fp16, 2^-8 for
+# bf16) before the FP32-accumulated products, which perturbs each term of the
+# dV, dK and dQ contractions by at most about 2u relative.  What is assumed:
+# that the sum of a gradient entry's absolute terms stays within 2x of the
+# largest gradient entry (cancellation can break this), which gives
+# max |G - G_ref| <= 4u * max(1, max |G_ref|); measurement, not proof,
+# supports it.
 BWD_REL = {"f16": 4 * 2.0 ** -11, "bf16": 4 * 2.0 ** -8}
