@@ -530,7 +530,7 @@ def profile_bwd(launches=10):
 
 
 def ceiling(seconds=3.0, pairs=2000):
-    """Sustained TFLOP/s, clock and power of the ceiling probe's six mixes,
+    """Sustained TFLOP/s, clock and power of the ceiling probe's seven mixes,
     of attn_fwd on C4 and C5 and attn_bwd on C4, then the HBM probes beside
     row_softmax (R2) and paged_decode (D32), one after the other in this
     process."""
@@ -560,7 +560,8 @@ def ceiling(seconds=3.0, pairs=2000):
              (2, "MFMA + LDS read + fma, exp2, add, 1/2 fp16 pack per MFMA"),
              (3, "MFMA + LDS read + 2 x (fma, exp2, add), 1 fp16 pack per MFMA"),
              (4, "mix 2 at one wave per SIMD"),
-             (5, "mix 2 at one wave per SIMD, each LDS fragment feeding two MFMAs"))
+             (5, "mix 2 at one wave per SIMD, each LDS fragment feeding two MFMAs"),
+             (6, "mix 2 in phases: a step's 16 MFMAs, then its 16 values (two waves per SIMD)"))
     rows = []
     for mix, desc in mixes:
         flops = float(grid) * lib.osc_ceiling_mfma_per_wg_iter(mix) * pairs * 32768.0

@@ -22,7 +22,11 @@
 //   mix 4  mix 2 with one wave per SIMD (256-thread workgroups);
 //   mix 5  mix 4 with each LDS fragment feeding two MFMAs (two B operands,
 //          as a wave holding two 32-row query blocks would): half the LDS
-//          reads per MFMA, the same softmax work per MFMA.
+//          reads per MFMA, the same softmax work per MFMA;
+//   mix 6  mix 2's instructions in phases, as a kernel that finishes a
+//          tile's products before its softmax orders them: each step's 16
+//          MFMAs back to back, then the 16 values of that step's scores (two
+//          waves per SIMD).
 // bench.py runs each mix back to back while sampling clock and power.
 //
 // Two HBM probes give the same kind of reference for the memory-bound paths:
@@ -46,7 +50,7 @@ constexpr int kLdsVec = 6144;  // 96 KiB of 16-byte vectors: one workgroup per C
 constexpr int kMfmaPerIter = 16;
 
 // Threads per workgroup: two waves per SIMD, or one for mixes 4 and 5.
-constexpr int threads_of(int mix) { return mix >= 4 ? 256 : 512; }
+constexpr int threads_of(int mix) { return mix == 4 || mix == 5 ? 256 : 512; }
 
 // One step: 16 MFMAs into accumulator set PH; with MIX >= 1 their A operands
 // come from a ring of 4 LDS fragments, each read 4 fragments ahead of its
@@ -89,6 +93,35 @@ __device__ __forceinline__ void ceiling_step(f32x16 (&c)[2][4], f16x8 (&ring)[4]
     }
 }
 
+// Mix 6: the 16 MFMAs of a step back to back (A operands through the same
+// 4-deep LDS ring), then the softmax work on 16 values of the scores those
+// MFMAs just produced, with no MFMA beside it.
+template <int PH>
+__device__ __forceinline__ void phased_step(f32x16 (&c)[2][4], f16x8 (&ring)[4], const f16x8& b0,
+                                            const f16x8 __attribute__((address_space(3)))* base,
+                                            float& sum, float& p0) {
+#pragma unroll
+    for (int m = 0; m < kMfmaPerIter; ++m) {
+        c[PH][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ring[m & 3], b0, c[PH][m & 3], 0, 0, 0);
+        ring[m & 3] = base[256 * ((m + 4) & 15)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < kMfmaPerIter; ++x) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(c[PH][x >> 3][x & 7], 1.0e-4f, -0.5f));
+        sum += p;
+        if (x & 1) {
+            f16x2 pk;
+            pk[0] = (_Float16)p0;
+            pk[1] = (_Float16)p;
+            asm volatile("" ::"v"(pk));
+        } else {
+            p0 = p;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int MIX>
 __global__ void __launch_bounds__(threads_of(MIX), 1)
 ceiling_kernel(const f16x8* __restrict__ src, float* __restrict__ out, int pairs) {
@@ -118,8 +151,13 @@ ceiling_kernel(const f16x8* __restrict__ src, float* __restrict__ out, int pairs
     for (int it = 0; it < pairs; ++it) {
         // Opaque per iteration, so the LDS reads are not hoisted out of the loop.
         asm volatile("" : "+v"(base));
-        ceiling_step<MIX, 0>(c, ring, a, b0, b1, base, sum, p0);
-        ceiling_step<MIX, 1>(c, ring, a, b0, b1, base, sum, p0);
+        if constexpr (MIX == 6) {
+            phased_step<0>(c, ring, b0, base, sum, p0);
+            phased_step<1>(c, ring, b0, base, sum, p0);
+        } else {
+            ceiling_step<MIX, 0>(c, ring, a, b0, b1, base, sum, p0);
+            ceiling_step<MIX, 1>(c, ring, a, b0, b1, base, sum, p0);
+        }
     }
     float r = sum;
 #pragma unroll
@@ -184,19 +222,19 @@ extern "C" {
 int64_t osc_ceiling_src_bytes() { return (int64_t)kLdsVec * 16; }
 
 // MFMAs one launch of mix `mix` issues per workgroup and iteration (x 32768
-// FLOP each); 0 for a mix outside 0 to 5.
+// FLOP each); 0 for a mix outside 0 to 6.
 int osc_ceiling_mfma_per_wg_iter(int mix) {
-    if (mix < 0 || mix > 5) return 0;
+    if (mix < 0 || mix > 6) return 0;
     return (threads_of(mix) / 64) * 2 * kMfmaPerIter;
 }
 
-// Enqueue one launch of mix `mix` (0 to 5) on `stream`: `grid` workgroups of
+// Enqueue one launch of mix `mix` (0 to 6) on `stream`: `grid` workgroups of
 // `iters` iterations (of 2 x 16 MFMAs per wave) each.  src: device buffer of
 // osc_ceiling_src_bytes() bytes; out: device buffer of grid * 512 floats.
 // Returns a hipError_t value (hipErrorInvalidValue for a bad argument,
 // nothing enqueued).
 int osc_ceiling_launch(int mix, const void* src, float* out, int grid, int iters, hipStream_t stream) {
-    if (!src || !out || grid < 1 || iters < 1 || mix < 0 || mix > 5) return (int)hipErrorInvalidValue;
+    if (!src || !out || grid < 1 || iters < 1 || mix < 0 || mix > 6) return (int)hipErrorInvalidValue;
     const f16x8* s = static_cast<const f16x8*>(src);
     void* params[] = {(void*)&s, (void*)&out, (void*)&iters};
     const void* fns[] = {reinterpret_cast<const void*>(&ceiling_kernel<0>),
@@ -204,7 +242,8 @@ int osc_ceiling_launch(int mix, const void* src, float* out, int grid, int iters
                          reinterpret_cast<const void*>(&ceiling_kernel<2>),
                          reinterpret_cast<const void*>(&ceiling_kernel<3>),
                          reinterpret_cast<const void*>(&ceiling_kernel<4>),
-                         reinterpret_cast<const void*>(&ceiling_kernel<5>)};
+                         reinterpret_cast<const void*>(&ceiling_kernel<5>),
+                         reinterpret_cast<const void*>(&ceiling_kernel<6>)};
     return (int)hipLaunchKernel(fns[mix], dim3((unsigned)grid), dim3(threads_of(mix)), params, 0, stream);
 }
 

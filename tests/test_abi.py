@@ -53,10 +53,10 @@ def test_ceiling_probe_library_loads_and_rejects_bad_arguments():
                                        ctypes.c_int, ctypes.c_void_p]
     assert lib.osc_ceiling_src_bytes() == 6144 * 16
     lib.osc_ceiling_mfma_per_wg_iter.argtypes = [ctypes.c_int]
-    # Mixes 0-3: 8 waves; 4 and 5: 4 waves; 32 MFMAs per wave and iteration.
-    assert [lib.osc_ceiling_mfma_per_wg_iter(m) for m in range(-1, 7)] == [0, 256, 256, 256, 256, 128, 128, 0]
+    # Mixes 0-3 and 6: 8 waves; 4 and 5: 4 waves; 32 MFMAs per wave and iteration.
+    assert [lib.osc_ceiling_mfma_per_wg_iter(m) for m in range(-1, 8)] == [0, 256, 256, 256, 256, 128, 128, 256, 0]
     invalid = 1  # hipErrorInvalidValue
-    for mix, src, out, grid, iters in ((6, BASE, BASE, 1, 1), (-1, BASE, BASE, 1, 1),
+    for mix, src, out, grid, iters in ((7, BASE, BASE, 1, 1), (-1, BASE, BASE, 1, 1),
                                        (0, None, BASE, 1, 1), (0, BASE, None, 1, 1),
                                        (0, BASE, BASE, 0, 1), (0, BASE, BASE, 1, 0)):
         assert lib.osc_ceiling_launch(mix, src, out, grid, iters, None) == invalid
