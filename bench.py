@@ -889,10 +889,15 @@ def summarize_trace(trace_dir, out_path, cmd, last):
             tail = [x[1] for x in d[-last:]]
             lines.append("%s: mean of the last %d launches (the timed steps) %.2f us" % (
                 name[:110], len(tail), sum(tail) / len(tail) / 1e3))
-    lines.append("sources_sha256_16: attn_fwd.hip+mfma_tile.hpp+online_merge.hpp %s, "
-                 "decode.hip %s, splitkv.hip %s, bwd.hip %s" % (
-                     kernel_source_hash(), kernel_source_hash(("decode.hip",)),
-                     kernel_source_hash(("splitkv.hip",)), kernel_source_hash(("bwd.hip",))))
+    # Hashes of the sources of the kernels in this trace.
+    groups = ((is_fwd_kernel, ("attn_fwd.hip", "mfma_tile.hpp", "online_merge.hpp")),
+              (lambda n: "splitkv_merge" in n, ("splitkv.hip", "online_merge.hpp")),
+              (lambda n: "paged_decode" in n, ("decode.hip", "mfma_tile.hpp", "online_merge.hpp")),
+              (lambda n: "softmax" in n, ("row_softmax.hip", "online_merge.hpp")),
+              (lambda n: "attn_bwd" in n, ("bwd.hip", "mfma_tile.hpp", "online_merge.hpp")))
+    parts = ["%s %s" % ("+".join(srcs), kernel_source_hash(srcs))
+             for match, srcs in groups if any(match(n) for n in durs)]
+    lines.append("sources_sha256_16: " + ", ".join(parts))
     lines.append("")
     with open(out_path, "w") as f:
         f.write("\n".join(lines))
