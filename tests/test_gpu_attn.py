@@ -93,6 +93,31 @@ def test_configs_sampled_rows(wname):
     check(wname + " sampled", o_rows, lse_rows, o_ref, lse_ref, w.dtype)
 
 
+LONG = [
+    # (B, H, N, D, causal, dtype): a million-token causal head at D = 128 (the
+    # 8-wave pipeline kernel, 4096 workgroups) and a ragged half-million-token
+    # non-causal pair at D = 64 (the unit kernel, two row blocks per wave);
+    # within-head offsets reach N*D = 2^27.
+    (1, 1, 1 << 20, 128, True, "f16"),
+    (1, 2, (1 << 19) + 37, 64, False, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", LONG, ids=lambda s: "B%dH%dN%dD%d_%s_%s" % (
+    s[0], s[1], s[2], s[3], "causal" if s[4] else "full", s[5]))
+def test_long_sequences_sampled_rows(shape):
+    """Very long sequences: sampled rows (first and last rows, tile edges,
+    random rows) against the oracle, and every element finite."""
+    B, H, N, D, causal, dtype = shape
+    print("running long sequence", shape, flush=True)
+    q, k, v = workloads.attn_inputs(B, H, N, D, dtype, seed=N % 1000 + D)
+    o, lse = run_gpu(q, k, v, causal, dtype)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = workloads.sample_rows(B, H, N, 48, seed=N % 997)
+    o_ref, lse_ref = oracle.attn_rows(q, k, v, causal, rows)
+    check("long %s" % (shape,), o.reshape(-1, D)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, dtype)
+
+
 def test_causal_prefix_is_bit_exact():
     """Changing keys/values after row i leaves rows <= i bit-identical (masked keys contribute 0)."""
     B, H, N, D = 1, 2, 700, 128
