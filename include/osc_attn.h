@@ -342,8 +342,13 @@ int64_t attn_bwd_workspace(int64_t B, int64_t H, int64_t N);
  *   x   [M, N] FP32 input, row-major, 4-byte aligned (rows need not be
  *       16-byte aligned; misaligned row starts are handled inside).
  *   y   [M, N] FP32 output, same layout; must not overlap x.
- *   M   number of rows (>= 1);  N  row length (>= 1);  M*N < 2^62.
+ *   M   number of rows, 1 <= M < 2^31;  N  row length, 1 <= N < 2^31;
+ *       M*N < 2^62.
  *   stream  HIP stream to enqueue on.
+ *
+ * Errors: x or y NULL ATTN_ERR_NULL; a size outside the limits above
+ * ATTN_ERR_SHAPE; x or y not 4-byte aligned ATTN_ERR_ALIGN; x and y
+ * overlapping ATTN_ERR_ALIAS.  Nothing is enqueued on an error.
  */
 attn_status_t row_softmax(const float *x, float *y, int64_t M, int64_t N, hipStream_t stream);
 

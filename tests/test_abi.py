@@ -288,6 +288,8 @@ def test_softmax_rejections():
     assert call_softmax(M=0) == 2
     assert call_softmax(N=0) == 2
     assert call_softmax(M=1 << 40, N=1 << 30) == 2
+    assert call_softmax(M=1 << 31, N=1) == 2      # M < 2^31
+    assert call_softmax(M=1, N=1 << 31) == 2      # N < 2^31
     assert call_softmax(x=BASE + 2) == 4
     assert call_softmax(y=BASE + 64 * MB + 1) == 4
     assert call_softmax(y=BASE + 200) == 6

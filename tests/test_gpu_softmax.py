@@ -57,6 +57,15 @@ def test_row_lengths(N):
     check("M%d N%d" % (M, N), run_gpu(x), oracle.row_softmax(x))
 
 
+@pytest.mark.parametrize("M,N,x_off", [(2, (1 << 24) + 3, 1), (3, 1000003, 0)])
+def test_very_long_rows(M, N, x_off):
+    """Rows of millions of elements (the streaming kernel), one of them with
+    misaligned row starts: every element against the oracle."""
+    x = workloads.softmax_inputs(M, N, seed=400 + M, last=None) * 4
+    print("running row_softmax very long M%d N%d x_off %d" % (M, N, x_off), flush=True)
+    check("long M%d N%d" % (M, N), run_gpu(x, x_off, 0), oracle.row_softmax(x))
+
+
 @pytest.mark.parametrize("x_off,y_off", [(1, 1), (2, 2), (3, 3), (1, 3), (0, 2), (3, 0)])
 @pytest.mark.parametrize("N", [6, 257, 3001, 9000])
 def test_misaligned_rows(N, x_off, y_off):
