@@ -101,8 +101,10 @@ typedef enum {
  *   dtype    ATTN_F16 or ATTN_BF16, the storage type of q, k and v.
  *   stream   HIP stream to enqueue on.
  *
- * Limits: N*D < 2^31 and B*H*N*D < 2^62.  o and lse must not overlap q, k, v
- * or each other.  The softmax scale is fixed at 1/sqrt(D).
+ * Limits: N*D < 2^31, B*H < 2^31, B*H*ceil(N/128) < 2^31 (the workgroup
+ * count) and B*H*N*D < 2^62; other sizes ATTN_ERR_SHAPE.  o and lse must
+ * not overlap q, k, v or each other.  The softmax scale is fixed at
+ * 1/sqrt(D).
  */
 attn_status_t attn_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
                        int64_t B, int64_t H, int64_t N, int64_t D, int causal,
@@ -215,7 +217,9 @@ int64_t attn_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t N, int64_t D, i
  * lengths and block_table are device data, which the call does not read:
  * a request whose length is out of range, or which uses a page id out of
  * range, gets NaN in all of its o and lse entries (no out-of-range address is
- * read).  Limits: P*2*T*Hkv*D < 2^62, max_pages*T < 2^31, B*max_pages < 2^31.
+ * read).  Limits: P*2*T*Hkv*D < 2^62, P < 2^31, max_pages*T < 2^31,
+ * B*max_pages < 2^31, B*Hq < 2^31, and B*Hkv times the number of segments
+ * below 2^31 (the workgroup count); other sizes ATTN_ERR_SHAPE.
  * o, lse and the workspace must not overlap the inputs or each other.
  */
 attn_status_t paged_decode(const void *q, const void *cache, const int32_t *block_table,

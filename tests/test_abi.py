@@ -82,7 +82,9 @@ def test_attn_rejects_null(field):
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(D=0), dict(N=-5),
-                                dict(N=1 << 24), dict(B=1 << 40, H=1 << 30)])
+                                dict(N=1 << 24), dict(B=1 << 40, H=1 << 30),
+                                dict(B=1 << 16, H=1 << 15, N=1),          # B*H = 2^31
+                                dict(B=1 << 20, H=1 << 4, N=1 << 14)])    # 2^31 workgroups
 def test_attn_rejects_bad_shapes(kw):
     assert call_attn(**kw) == 2
 
@@ -209,6 +211,8 @@ def test_paged_decode_rejections():
     assert call_decode(B=0) == 2
     assert call_decode(Hq=30) == 2
     assert call_decode(splits=-3) == 2
+    assert call_decode(B=1 << 16, Hq=1 << 15, Hkv=1 << 15, max_pages=1) == 2   # B*Hq = 2^31
+    assert call_decode(P=1 << 31, T=1, Hkv=1, Hq=1, D=64) == 2              # P = 2^31
     assert call_decode(D=80) == 3
     assert call_decode(T=24) == 3
     assert call_decode(Hq=64, Hkv=1) == 3            # group of 64 heads
