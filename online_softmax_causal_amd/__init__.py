@@ -33,13 +33,15 @@ expects (q, k, v, dout and the cache in the 16-bit `dtype`; o, lse and the
 gradients FP32; block_table and lengths int32) and hold at least as many
 elements as the sizes imply; otherwise ValueError is raised.  (A CPU tensor
 would hand the kernel a host address, and a short buffer would be written past
-its end.)  An integer address is passed through unchecked.  ``stream`` accepts None (PyTorch's current stream on
-the current device), a ``torch.cuda.Stream`` or an integer handle.  A nonzero
+its end.)  An integer address is passed through unchecked.  The C call runs
+with the tensors' device made current.  ``stream`` accepts None (PyTorch's
+current stream on that device), a ``torch.cuda.Stream`` or an integer handle.  A nonzero
 status raises ``AttnError``.  ``attention(q, k, v, causal)`` is a convenience
 wrapper that allocates O and LSE with PyTorch and calls ``attn_fwd``.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -128,7 +130,8 @@ def _ptr(x):
 
 
 def _check(where, args):
-    """Validate the tensor arguments of one call before any launch.
+    """Validate the tensor arguments of one call before any launch; returns
+    their common device (None if every argument is an address or None).
 
     args: (name, value, kind, numel) with kind "h" (the 16-bit dtype of the
     call), "f32" or "i32"; numel the element count the sizes imply.  Integer
@@ -164,6 +167,7 @@ def _check(where, args):
             dev = t.device
         elif t.device != dev:
             raise ValueError("%s: %s is on %s, other arguments on %s" % (where, name, t.device, dev))
+    return dev
 
 
 def _check_half_dtype(where, dtype, tensors):
@@ -176,10 +180,20 @@ def _check_half_dtype(where, dtype, tensors):
             raise ValueError("%s: %s is %s but dtype says %s" % (where, name, t.dtype, td))
 
 
-def _stream(s):
+def _on(dev):
+    """The context a call runs in: the device of its tensors made current (the
+    library launches on the current device and keeps its per-device state
+    there); no change when every argument is a raw address."""
+    if dev is None:
+        return contextlib.nullcontext()
+    import torch
+    return torch.cuda.device(dev)
+
+
+def _stream(s, dev=None):
     if s is None:
         import torch
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(dev).cuda_stream
     if isinstance(s, int):
         return s
     if hasattr(s, "cuda_stream"):
@@ -205,10 +219,11 @@ def attn_fwd(q, k, v, o, lse, B, H, N, D, causal, dtype, stream=None) -> None:
     """Enqueue attention forward (see include/osc_attn.h); raises AttnError on a bad status."""
     n = int(B) * int(H) * int(N)
     _check_half_dtype("attn_fwd", dtype, [("q", q), ("k", k), ("v", v)])
-    _check("attn_fwd", [("q", q, "h", n * int(D)), ("k", k, "h", n * int(D)), ("v", v, "h", n * int(D)),
-                        ("o", o, "f32", n * int(D)), ("lse", lse, "f32", n)])
-    st = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N),
-                         int(D), int(bool(causal)), _dtype(dtype), _stream(stream))
+    dev = _check("attn_fwd", [("q", q, "h", n * int(D)), ("k", k, "h", n * int(D)), ("v", v, "h", n * int(D)),
+                              ("o", o, "f32", n * int(D)), ("lse", lse, "f32", n)])
+    with _on(dev):
+        st = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N),
+                             int(D), int(bool(causal)), _dtype(dtype), _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_fwd")
 
@@ -217,12 +232,13 @@ def attn_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, stream=None) -
     """Enqueue grouped-query attention forward (K/V have Hkv heads, Hkv divides H)."""
     n, nk = int(B) * int(H) * int(N), int(B) * int(Hkv) * int(N)
     _check_half_dtype("attn_fwd_gqa", dtype, [("q", q), ("k", k), ("v", v)])
-    _check("attn_fwd_gqa", [("q", q, "h", n * int(D)), ("k", k, "h", nk * int(D)),
-                            ("v", v, "h", nk * int(D)), ("o", o, "f32", n * int(D)),
-                            ("lse", lse, "f32", n)])
-    st = load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
-                             int(Hkv), int(N), int(D), int(bool(causal)), _dtype(dtype),
-                             _stream(stream))
+    dev = _check("attn_fwd_gqa", [("q", q, "h", n * int(D)), ("k", k, "h", nk * int(D)),
+                                  ("v", v, "h", nk * int(D)), ("o", o, "f32", n * int(D)),
+                                  ("lse", lse, "f32", n)])
+    with _on(dev):
+        st = load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                 int(Hkv), int(N), int(D), int(bool(causal)), _dtype(dtype),
+                                 _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_fwd_gqa")
 
@@ -238,14 +254,15 @@ def attn_fwd_splitkv(q, k, v, o, lse, B, H, Hkv, N, D, causal, dtype, num_splits
     """Enqueue split-KV attention forward (partial states in `workspace`, then a merge)."""
     n, nk = int(B) * int(H) * int(N), int(B) * int(Hkv) * int(N)
     _check_half_dtype("attn_fwd_splitkv", dtype, [("q", q), ("k", k), ("v", v)])
-    _check("attn_fwd_splitkv", [("q", q, "h", n * int(D)), ("k", k, "h", nk * int(D)),
-                                ("v", v, "h", nk * int(D)), ("o", o, "f32", n * int(D)),
-                                ("lse", lse, "f32", n),
-                                ("workspace", workspace, "bytes", max(0, int(workspace_bytes)))])
-    st = load().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
-                                 int(Hkv), int(N), int(D), int(bool(causal)), _dtype(dtype),
-                                 int(num_splits), _ptr(workspace), int(workspace_bytes),
-                                 _stream(stream))
+    dev = _check("attn_fwd_splitkv", [("q", q, "h", n * int(D)), ("k", k, "h", nk * int(D)),
+                                      ("v", v, "h", nk * int(D)), ("o", o, "f32", n * int(D)),
+                                      ("lse", lse, "f32", n),
+                                      ("workspace", workspace, "bytes", max(0, int(workspace_bytes)))])
+    with _on(dev):
+        st = load().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                     int(Hkv), int(N), int(D), int(bool(causal)), _dtype(dtype),
+                                     int(num_splits), _ptr(workspace), int(workspace_bytes),
+                                     _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_fwd_splitkv")
 
@@ -261,16 +278,18 @@ def paged_decode(q, cache, block_table, lengths, o, lse, B, Hq, Hkv, D, page_siz
     """Enqueue one paged grouped-query decode step (block_table, lengths: int32 device)."""
     nq = int(B) * int(Hq)
     _check_half_dtype("paged_decode", dtype, [("q", q), ("cache", cache)])
-    _check("paged_decode", [("q", q, "h", nq * int(D)),
-                            ("cache", cache, "h", int(num_pages) * 2 * int(page_size) * int(Hkv) * int(D)),
-                            ("block_table", block_table, "i32", int(B) * int(max_pages)),
-                            ("lengths", lengths, "i32", int(B)), ("o", o, "f32", nq * int(D)),
-                            ("lse", lse, "f32", nq),
-                            ("workspace", workspace, "bytes", max(0, int(workspace_bytes)))])
-    st = load().paged_decode(_ptr(q), _ptr(cache), _ptr(block_table), _ptr(lengths), _ptr(o),
-                             _ptr(lse), int(B), int(Hq), int(Hkv), int(D), int(page_size),
-                             int(num_pages), int(max_pages), _dtype(dtype), int(num_splits),
-                             _ptr(workspace), int(workspace_bytes), _stream(stream))
+    dev = _check("paged_decode", [("q", q, "h", nq * int(D)),
+                                  ("cache", cache, "h",
+                                   int(num_pages) * 2 * int(page_size) * int(Hkv) * int(D)),
+                                  ("block_table", block_table, "i32", int(B) * int(max_pages)),
+                                  ("lengths", lengths, "i32", int(B)), ("o", o, "f32", nq * int(D)),
+                                  ("lse", lse, "f32", nq),
+                                  ("workspace", workspace, "bytes", max(0, int(workspace_bytes)))])
+    with _on(dev):
+        st = load().paged_decode(_ptr(q), _ptr(cache), _ptr(block_table), _ptr(lengths), _ptr(o),
+                                 _ptr(lse), int(B), int(Hq), int(Hkv), int(D), int(page_size),
+                                 int(num_pages), int(max_pages), _dtype(dtype), int(num_splits),
+                                 _ptr(workspace), int(workspace_bytes), _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "paged_decode")
 
@@ -281,15 +300,16 @@ def paged_decode_noalloc(q, cache, block_table, lengths, o, lse, B, Hq, Hkv, D, 
     fixed per-device array of PAGED_NOALLOC_SCRATCH_BYTES bytes."""
     nq = int(B) * int(Hq)
     _check_half_dtype("paged_decode_noalloc", dtype, [("q", q), ("cache", cache)])
-    _check("paged_decode_noalloc", [
+    dev = _check("paged_decode_noalloc", [
         ("q", q, "h", nq * int(D)),
         ("cache", cache, "h", int(num_pages) * 2 * int(page_size) * int(Hkv) * int(D)),
         ("block_table", block_table, "i32", int(B) * int(max_pages)),
         ("lengths", lengths, "i32", int(B)), ("o", o, "f32", nq * int(D)), ("lse", lse, "f32", nq)])
-    st = load().paged_decode_noalloc(_ptr(q), _ptr(cache), _ptr(block_table), _ptr(lengths),
-                                     _ptr(o), _ptr(lse), int(B), int(Hq), int(Hkv), int(D),
-                                     int(page_size), int(num_pages), int(max_pages), _dtype(dtype),
-                                     int(num_splits), _stream(stream))
+    with _on(dev):
+        st = load().paged_decode_noalloc(_ptr(q), _ptr(cache), _ptr(block_table), _ptr(lengths),
+                                         _ptr(o), _ptr(lse), int(B), int(Hq), int(Hkv), int(D),
+                                         int(page_size), int(num_pages), int(max_pages), _dtype(dtype),
+                                         int(num_splits), _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "paged_decode_noalloc")
 
@@ -299,10 +319,10 @@ def _check_bwd(where, q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, dtype,
     n, nk = int(B) * int(H) * int(N), int(B) * int(Hkv) * int(N)
     d = int(D)
     _check_half_dtype(where, dtype, [("q", q), ("k", k), ("v", v), ("dout", dout)])
-    _check(where, [("q", q, "h", n * d), ("k", k, "h", nk * d), ("v", v, "h", nk * d),
-                   ("o", o, "f32", n * d), ("lse", lse, "f32", n), ("dout", dout, "h", n * d),
-                   ("dq", dq, "f32", n * d), ("dk", dk, "f32", nk * d), ("dv", dv, "f32", nk * d),
-                   ("workspace", workspace, "bytes", max(0, int(workspace_bytes)))])
+    return _check(where, [("q", q, "h", n * d), ("k", k, "h", nk * d), ("v", v, "h", nk * d),
+                          ("o", o, "f32", n * d), ("lse", lse, "f32", n), ("dout", dout, "h", n * d),
+                          ("dq", dq, "f32", n * d), ("dk", dk, "f32", nk * d), ("dv", dv, "f32", nk * d),
+                          ("workspace", workspace, "bytes", max(0, int(workspace_bytes)))])
 
 
 def attn_bwd_workspace(B, H, N) -> int:
@@ -313,11 +333,12 @@ def attn_bwd_workspace(B, H, N) -> int:
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, dtype, workspace,
              workspace_bytes, stream=None) -> None:
     """Enqueue attention backward (dq, dk, dv FP32) from the forward's o and lse."""
-    _check_bwd("attn_bwd", q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, D, dtype, workspace,
-               workspace_bytes)
-    st = load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                         _ptr(dk), _ptr(dv), int(B), int(H), int(N), int(D), int(bool(causal)),
-                         _dtype(dtype), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    dev = _check_bwd("attn_bwd", q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, D, dtype,
+                     workspace, workspace_bytes)
+    with _on(dev):
+        st = load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                             _ptr(dk), _ptr(dv), int(B), int(H), int(N), int(D), int(bool(causal)),
+                             _dtype(dtype), _ptr(workspace), int(workspace_bytes), _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_bwd")
 
@@ -325,20 +346,22 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, causal, dtype, works
 def attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, causal, dtype, workspace,
                  workspace_bytes, stream=None) -> None:
     """Enqueue attention backward with Hkv shared K/V heads (k, v, dk, dv [B, Hkv, N, D])."""
-    _check_bwd("attn_bwd_gqa", q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, dtype, workspace,
-               workspace_bytes)
-    st = load().attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                             _ptr(dk), _ptr(dv), int(B), int(H), int(Hkv), int(N), int(D),
-                             int(bool(causal)), _dtype(dtype), _ptr(workspace),
-                             int(workspace_bytes), _stream(stream))
+    dev = _check_bwd("attn_bwd_gqa", q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, D, dtype,
+                     workspace, workspace_bytes)
+    with _on(dev):
+        st = load().attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), int(B), int(H), int(Hkv), int(N), int(D),
+                                 int(bool(causal)), _dtype(dtype), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "attn_bwd_gqa")
 
 
 def row_softmax(x, y, M, N, stream=None) -> None:
     """Enqueue the row softmax of an FP32 [M, N] matrix; raises AttnError on a bad status."""
-    _check("row_softmax", [("x", x, "f32", int(M) * int(N)), ("y", y, "f32", int(M) * int(N))])
-    st = load().row_softmax(_ptr(x), _ptr(y), int(M), int(N), _stream(stream))
+    dev = _check("row_softmax", [("x", x, "f32", int(M) * int(N)), ("y", y, "f32", int(M) * int(N))])
+    with _on(dev):
+        st = load().row_softmax(_ptr(x), _ptr(y), int(M), int(N), _stream(stream, dev))
     if st != 0:
         raise AttnError(st, "row_softmax")
 

@@ -383,3 +383,12 @@ def test_binding_rejects_wrong_dtypes_and_layouts():
         with pytest.raises(ValueError, match="elements, the sizes need"):
             osc.attn_bwd(_f16(n), _f16(n), _f16(n), _f32(n), _f32(B * H * N), _f16(n), g["dq"], g["dk"],
                          g["dv"], B, H, N, D, True, "f16", _f32(64), 256, 0)
+
+
+def test_binding_calls_run_on_the_tensors_device():
+    """The binding runs each C call with its tensors' device made current and
+    that device's stream: _check reports the common device (None when every
+    argument is a raw address, which then runs in the caller's context)."""
+    assert osc._check("t", [("a", BASE, "f32", 4), ("b", None, "f32", 4)]) is None
+    with osc._on(None):
+        pass
