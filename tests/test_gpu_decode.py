@@ -62,6 +62,10 @@ CASES = [
     (2, 16, 2, 128, 8, (513, 2048), 1),
     (5, 6, 3, 64, 32, (1, 2, 600, 95, 2500), 7),
     (1, 2, 2, 128, 2, (4097,), 0),
+    # large pages: 1024 tokens, and the largest page size, 65536 tokens, with
+    # a request of two full pages and one that ends one token into a page
+    (2, 8, 2, 64, 1024, (3000, 1025), 0),
+    (2, 4, 1, 64, 65536, (131072, 65537), 0),
 ]
 
 
