@@ -531,9 +531,9 @@ def profile_bwd(launches=10):
 
 def ceiling(seconds=3.0, pairs=2000):
     """Sustained TFLOP/s, clock and power of the ceiling probe's seven mixes,
-    of attn_fwd on C4 and C5 and attn_bwd on C4, then the HBM probes beside
-    row_softmax (R2) and paged_decode (D32), one after the other in this
-    process."""
+    of attn_fwd on C4 and C5 and attn_bwd on C4, the LDS read probe, then the
+    HBM probes beside row_softmax (R2) and paged_decode (D32), one after the
+    other in this process."""
     import ctypes
     import torch
     import online_softmax_causal_amd as osc
@@ -605,6 +605,29 @@ def ceiling(seconds=3.0, pairs=2000):
                  measure_clock(bwd, 2.5 * w.flops, seconds)))
     del q, k, v, do, o, lse, grads, ws
 
+    # LDS: fragment reads alone, 16 KiB per wave and iteration; bytes per
+    # clock per CU at the sampled clock.
+    lib.osc_lds_read_launch.restype = ctypes.c_int
+    lib.osc_lds_read_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lout = torch.empty(grid * 512, dtype=torch.int32, device=dev)
+    lds_rows = []
+    for tr, waves, desc in ((0, 8, "ds_read_b128 rows, two waves per SIMD"),
+                            (0, 4, "ds_read_b128 rows, one wave per SIMD"),
+                            (1, 8, "ds_read_b64_tr_b16 pairs (V^T fragments), two waves per SIMD"),
+                            (1, 4, "ds_read_b64_tr_b16 pairs (V^T fragments), one wave per SIMD")):
+        iters = 4000
+
+        def lread(tr=tr, waves=waves, iters=iters):
+            e = lib.osc_lds_read_launch(tr, waves, src.data_ptr(), lout.data_ptr(), grid, iters, stream)
+            if e != 0:
+                raise RuntimeError("LDS probe launch failed: %d" % e)
+        for _ in range(5):
+            lread()
+        torch.cuda.synchronize()
+        lds_rows.append((desc, measure_clock(lread, float(grid) * waves * iters * 16384.0, seconds)))
+    del lout
+
     # HBM: streaming read and copy of 1 GiB, then the row softmax (R2) and the
     # 32K-token paged decode (D32), each timed the same way (bytes per second).
     lib.osc_hbm_read_launch.restype = ctypes.c_int
@@ -674,6 +697,14 @@ def ceiling(seconds=3.0, pairs=2000):
         print("%s | %.1f | %.1f | %.0f | %.0f | %.1f" % (
             desc, c["sustained_tflops"], 100.0 * c["sustained_tflops"] / PEAK_F16_TFLOPS, c["clock_mhz"],
             c["power_w"] or float("nan"), 100.0 * c["frac_of_peak_at_clock"]))
+    print("")
+    print("LDS fragment reads alone | B per clock per CU | GFX MHz | W")
+    for desc, c in lds_rows:
+        if c is None:
+            print("%s | (amdsmi unavailable)" % desc)
+            continue
+        bpc = c["sustained_tflops"] * 1e12 / (256 * c["clock_mhz"] * 1e6)
+        print("%s | %.0f | %.0f | %.0f" % (desc, bpc, c["clock_mhz"], c["power_w"] or 0))
     print("")
     print("workload | TB/s | % of 8 TB/s | GFX MHz | W")
     for desc, c in hbm_rows:

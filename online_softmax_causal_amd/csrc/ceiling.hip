@@ -29,6 +29,11 @@
 //          waves per SIMD).
 // bench.py runs each mix back to back while sampling clock and power.
 //
+// An LDS probe streams fragment reads alone, as the MFMA operands are read:
+// 16-byte ds_read_b128 rows, or pairs of 8-byte ds_read_b64_tr_b16 transposed
+// reads in the attention kernels' swizzled layout, 1 KiB per wave
+// instruction pair or row read, with one or two waves per SIMD.
+//
 // Two HBM probes give the same kind of reference for the memory-bound paths:
 // a streaming read and a streaming copy, both grid-stride with 16-byte
 // non-temporal accesses.  Their shapes are the fastest of a sweep over grid
@@ -171,6 +176,65 @@ ceiling_kernel(const f16x8* __restrict__ src, float* __restrict__ out, int pairs
     out[(int64_t)blockIdx.x * 512 + tid] = r;
 }
 
+// LDS read probe: TR = 0 reads 16-byte rows (ds_read_b128, lane l reads
+// vector l of a 1 KiB block), TR = 1 reads pairs of transposed 8-byte
+// fragments (ds_read_b64_tr_b16) at the attention kernels' V^T fragment
+// offsets in a chunk-swizzled 64-row x 128-column tile.  Eight reads are in
+// flight per wave; each iteration reads 16 KiB per wave (16 x 1 KiB).
+template <int NT, int TR>
+__global__ void __launch_bounds__(NT, 1)
+lds_read_kernel(const u32x4* __restrict__ src, unsigned* __restrict__ out, int iters) {
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    __shared__ u32x4 lds[kLdsVec];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kLdsVec; i += NT) lds[i] = src[i];
+    __syncthreads();
+    const int lane = tid & 63;
+    // TR = 0: vector lane + 64 (16 b) of 1 KiB block b, b < 16.
+    const lds_u32x4* rb = (const lds_u32x4*)lds + lane;
+    // TR = 1: two 8-byte reads per fragment at the attention kernels' V^T
+    // fragment offsets in a 64 x 128 tile of 16-bit values (16-byte chunks
+    // XOR-swizzled by row): d block mt, rows 4 (lane / 32) + (lane / 4) % 4
+    // + 8 r of a 16-row group; fragment f is d block f / 4 of group f % 4.
+    const __attribute__((address_space(3))) short* tl = (const __attribute__((address_space(3))) short*)lds;
+    const lds_s16x4* tb[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int row = 4 * (lane >> 5) + ((lane >> 2) & 3) + 8 * r;
+            const int c = 4 * mt + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+            const int sw = ((row & 3) << 2) | ((row >> 2) & 3);
+            tb[mt][r] = (const lds_s16x4*)(tl + row * 128 + ((c ^ sw) << 3) + 4 * (lane & 1));
+        }
+    u32x4 acc = u32x4{0u, 0u, 0u, 0u};
+    for (int it = 0; it < iters; ++it) {
+        // Opaque per iteration, so the reads are not hoisted out of the loop.
+        asm volatile("" : "+v"(rb));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) asm volatile("" : "+v"(tb[mt][0]), "+v"(tb[mt][1]));
+        u32x4 x[16];
+#pragma unroll
+        for (int f = 0; f < 16; ++f) {
+            if constexpr (TR == 0) {
+                x[f] = rb[64 * f];
+            } else {
+                const int o = (f & 3) * 16 * 128 / 4;  // 16-row group, in 8-byte units
+                const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tb[f >> 2][0] + o));
+                const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tb[f >> 2][1] + o));
+                const auto lo = __builtin_bit_cast(unsigned long long, a);
+                const auto hi = __builtin_bit_cast(unsigned long long, b);
+                x[f] = u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi, (unsigned)(hi >> 32)};
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < 16; ++f) acc ^= x[f];
+    }
+    out[(int64_t)blockIdx.x * 512 + tid] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 constexpr int kHbmThreads = 256;
 
 constexpr int kReadInFlight = 8;   // loads per thread per round
@@ -245,6 +309,24 @@ int osc_ceiling_launch(int mix, const void* src, float* out, int grid, int iters
                          reinterpret_cast<const void*>(&ceiling_kernel<5>),
                          reinterpret_cast<const void*>(&ceiling_kernel<6>)};
     return (int)hipLaunchKernel(fns[mix], dim3((unsigned)grid), dim3(threads_of(mix)), params, 0, stream);
+}
+
+// LDS read probe: `grid` workgroups of `waves` waves (4 or 8: one or two per
+// SIMD), `iters` iterations of 16 KiB per wave, 16-byte row reads (tr = 0)
+// or transposed pairs (tr = 1).  src: device buffer of osc_ceiling_src_bytes()
+// bytes; out: grid * 512 unsigned.  Returns a hipError_t value
+// (hipErrorInvalidValue for a bad argument, nothing enqueued).
+int osc_lds_read_launch(int tr, int waves, const void* src, unsigned* out, int grid, int iters,
+                        hipStream_t stream) {
+    if (!src || !out || grid < 1 || iters < 1 || (tr != 0 && tr != 1) || (waves != 4 && waves != 8))
+        return (int)hipErrorInvalidValue;
+    const u32x4* s = static_cast<const u32x4*>(src);
+    void* params[] = {(void*)&s, (void*)&out, (void*)&iters};
+    const void* fn = tr == 0 ? (waves == 4 ? reinterpret_cast<const void*>(&lds_read_kernel<256, 0>)
+                                           : reinterpret_cast<const void*>(&lds_read_kernel<512, 0>))
+                             : (waves == 4 ? reinterpret_cast<const void*>(&lds_read_kernel<256, 1>)
+                                           : reinterpret_cast<const void*>(&lds_read_kernel<512, 1>));
+    return (int)hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * waves), params, 0, stream);
 }
 
 // Streaming read of `bytes` (a multiple of 16) from src: `grid` workgroups of

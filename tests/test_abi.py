@@ -60,6 +60,12 @@ def test_ceiling_probe_library_loads_and_rejects_bad_arguments():
                                        (0, None, BASE, 1, 1), (0, BASE, None, 1, 1),
                                        (0, BASE, BASE, 0, 1), (0, BASE, BASE, 1, 0)):
         assert lib.osc_ceiling_launch(mix, src, out, grid, iters, None) == invalid
+    lib.osc_lds_read_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    for tr, waves, src, out, grid, iters in ((2, 8, BASE, BASE, 1, 1), (0, 6, BASE, BASE, 1, 1),
+                                             (0, 8, None, BASE, 1, 1), (1, 4, BASE, None, 1, 1),
+                                             (0, 4, BASE, BASE, 0, 1), (1, 8, BASE, BASE, 1, 0)):
+        assert lib.osc_lds_read_launch(tr, waves, src, out, grid, iters, None) == invalid
 
 
 def test_status_strings():
