@@ -32,11 +32,14 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-# Per-source flags.  attn_fwd.hip: VGPR-form MFMAs, so the key-split kernel
-# (one wave per SIMD, where the compiler would otherwise give every MFMA AGPR
-# accumulators and copy the scores out) keeps its accumulators in VGPRs; the
-# file's other kernels compile to the same instructions with or without it.
-SRC_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source flags: VGPR-form MFMAs.  In attn_fwd.hip the key-split kernel,
+# and in bwd.hip the D = 128 dK/dV kernel, run one wave per SIMD; there the
+# compiler would otherwise give the S and dP products AGPR accumulators and
+# copy every score out with v_accvgpr_read (one per MFMA in the dK/dV loop).
+# The other kernels of attn_fwd.hip compile to the same instructions with or
+# without it.
+SRC_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+             "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
