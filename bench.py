@@ -718,7 +718,7 @@ def ceiling(seconds=3.0, pairs=2000):
     print("sources_sha256_16: ceiling.hip %s, attn_fwd.hip+mfma_tile.hpp+online_merge.hpp %s, "
           "row_softmax.hip %s, decode.hip %s"
           % (kernel_source_hash(("ceiling.hip",)), kernel_source_hash(),
-             kernel_source_hash(("row_softmax.hip",)), kernel_source_hash(("decode.hip",))))
+             kernel_source_hash(("row_softmax.hip",)), kernel_source_hash(("decode.hip", "decode_short.hip", "decode_kernel.hpp"))))
 
 
 def _pmc_rows(path):
@@ -923,7 +923,7 @@ def summarize_trace(trace_dir, out_path, cmd, last):
     # Hashes of the sources of the kernels in this trace.
     groups = ((is_fwd_kernel, ("attn_fwd.hip", "mfma_tile.hpp", "online_merge.hpp")),
               (lambda n: "splitkv_merge" in n, ("splitkv.hip", "online_merge.hpp")),
-              (lambda n: "paged_decode" in n, ("decode.hip", "mfma_tile.hpp", "online_merge.hpp")),
+              (lambda n: "paged_decode" in n, ("decode.hip", "decode_short.hip", "decode_kernel.hpp", "mfma_tile.hpp", "online_merge.hpp")),
               (lambda n: "softmax" in n, ("row_softmax.hip", "online_merge.hpp")),
               (lambda n: "attn_bwd" in n, ("bwd.hip", "mfma_tile.hpp", "online_merge.hpp")))
     parts = ["%s %s" % ("+".join(srcs), kernel_source_hash(srcs))

@@ -23,8 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libosc_attn.so")
 CEILING_LIB = os.path.join(PKG, "libosc_ceiling.so")
-SOURCES = ["attn_fwd.hip", "bwd.hip", "decode.hip", "splitkv.hip", "row_softmax.hip", "api.hip",
-           "noalloc.hip"]
+SOURCES = ["attn_fwd.hip", "bwd.hip", "decode.hip", "decode_short.hip", "splitkv.hip", "row_softmax.hip",
+           "api.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -37,9 +37,11 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
 # compiler would otherwise give the S and dP products AGPR accumulators and
 # copy every score out with v_accvgpr_read (one per MFMA in the dK/dV loop).
 # The other kernels of attn_fwd.hip compile to the same instructions with or
-# without it.
+# without it.  decode_short.hip is the decode kernel built this way, which
+# launch_paged_decode uses for short segments only.
 SRC_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-             "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+             "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+             "decode_short.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
@@ -86,7 +88,7 @@ def build(verbose: bool = False) -> str:
     probe's); returns the library's path."""
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 3) as ex:
-        m0 = [ex.submit(check_m0, src) for src in ("attn_fwd.hip", "decode.hip", "bwd.hip")]
+        m0 = [ex.submit(check_m0, src) for src in ("attn_fwd.hip", "decode.hip", "decode_short.hip", "bwd.hip")]
         ceiling = ex.submit(_compile, "ceiling.hip")
         objs = list(ex.map(_compile, SOURCES))
         for f in m0:
