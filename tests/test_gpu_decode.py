@@ -154,6 +154,30 @@ def test_deterministic_and_split_consistent():
     assert np.abs(l1 - l3).max() <= tolerances.ATTN_LSE
 
 
+# Segments of at most 512 tokens run the decode kernel's VGPR-form build, longer
+# ones the other build.  With 16-token pages and 64 pages per request (1024
+# tokens of capacity, 32 tiles of 32) the requested splits give segments of
+# 256 and 512 tokens (short build) and 1024 (long build, one segment); with 69
+# pages (1104 tokens, 35 tiles) two splits give 576-token segments (long build,
+# two segments).  Every plan against the oracle.
+@pytest.mark.parametrize("lens,splits", [((1008, 700), 4), ((1008, 700), 2), ((1008, 700), 1),
+                                         ((1080, 999), 2)],
+                         ids=["seg256", "seg512", "seg1024", "seg576"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_both_decode_builds_around_the_segment_boundary(lens, splits, dtype):
+    B, Hq, Hkv, D, T = 2, 16, 4, 128, 16
+    max_pages = (max(lens) + T - 1) // T + 1
+    P = B * max_pages + 3
+    seed = 7300 + sum(lens)
+    q, cache, bt, ln = workloads.decode_inputs(B, Hq, Hkv, D, T, P, max_pages, lens, dtype, seed,
+                                               sigma_qk=1.5)
+    name = "decode boundary %s lens %s splits %d seed %d" % (dtype, lens, splits, seed)
+    print("running", name, flush=True)
+    o, lse, _ = run_decode(q, cache, bt, ln, T, dtype, splits)
+    o_ref, lse_ref = oracle.paged_decode(q, cache, bt.numpy(), ln.numpy(), T)
+    check(name, o.reshape(-1, D), lse.reshape(-1), o_ref, lse_ref, dtype)
+
+
 @pytest.mark.parametrize("name", ["D1", "D32"])
 def test_benchmark_workload_sampled(name):
     """The benchmark's shapes (B8 Hq32 Hkv8 D128 page 16) in its launch
